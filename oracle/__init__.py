@@ -1,0 +1,37 @@
+"""CPU oracle for the LoopKV plan-driven quantized decode path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or
+constant generator with the HIP library under ``loop_aware_quantized_amd``;
+both sides receive the same seeded inputs and nothing else.
+
+What it follows (pages cited by title and section; no line numbers):
+
+* "LoopKV: Loop-Aware KV Cache Compression for Serving Looped Transformers",
+  abstract (概要 on the mlinfo page, "Full text" on the astralor page):
+  a KV cache kept per (loop, layer) cell; an offline plan gives each cell
+  4-bit storage, 2-bit storage, or reuse of the final loop's KV for that
+  layer; at decode each loop reads the high two bits of every 4-bit value
+  and fetches the low two bits only where its own attention weight needs
+  4-bit precision.
+* The related-papers list (関連論文リスト) on the fugumt LoopVQ page, KIVI
+  entry: tuning-free asymmetric low-bit KV quantization.  Its layout (keys
+  per channel over token groups, values per token over channel groups, with
+  a float scale and zero point) is the codec shape used here.
+
+Precision: the codec's defining steps are fp32/fp16 operations emulated
+exactly with numpy float32/float16, because they define stored bytes; every
+step after dequantization is float64.
+
+Modules
+-------
+codec      group quantizer, bit planes, 2-bit row packing
+cache      per-sequence cell cache and its paged byte layout
+attention  decode of one cell: scores, softmax, tau mask, output
+
+Parity status of every function is listed in each module's header.  No
+function here is "parity unpinned": each is pinned by tests under
+``tests/test_oracle_*.py`` to closed forms, brute force, a library routine or
+hand-derived fixtures in ``tests/golden``.
+"""
