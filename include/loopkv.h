@@ -1,0 +1,223 @@
+/*
+ * loopkv.h -- C ABI of the LoopKV plan-driven quantized decode library for
+ * MI355X (gfx950).
+ *
+ * What the library computes comes from "LoopKV: Loop-Aware KV Cache
+ * Compression for Serving Looped Transformers", abstract (概要):
+ *   - a looped transformer keeps one KV cache per (loop, layer) cell;
+ *   - a one-time offline plan stores each cell at 4 bits, at 2 bits, or as a
+ *     reuse of the final loop's KV of the same layer;
+ *   - while decoding, each loop reads the high two bits of every 4-bit value
+ *     and fetches the low two bits only where its own attention weights need
+ *     4-bit precision.
+ * The quantizer layout (keys per channel over token groups, values per token
+ * over channel groups, fp16 scale and zero point) follows the KIVI entry of
+ * the related-papers list on the fugumt LoopVQ page.
+ *
+ * Conventions for every call
+ *   - All pointers documented "device" are HIP device pointers owned by the
+ *     caller; "host" pointers are read during the call only.  The library
+ *     never allocates, frees or retains device memory.  It owns only the
+ *     host-side, immutable plan object.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Compute calls are asynchronous on that stream: launch errors are
+ *     reported by the return code, faults surface at the caller's next
+ *     synchronization.
+ *   - Return codes: 0 = LOOPKV_OK, > 0 = informational success,
+ *     < 0 = error with nothing launched.  loopkv_last_error() returns the
+ *     calling thread's last error message.  No call aborts or throws.
+ *   - Host-visible arguments are always validated.  Device-resident lengths
+ *     and block tables are trusted (an out-of-range entry is undefined
+ *     behaviour) unless the environment variable LOOPKV_DEBUG=1 is set, in
+ *     which case they are copied to the host and checked first (this
+ *     synchronizes the stream).
+ *   - The plan is immutable: concurrent calls on different streams are safe
+ *     when they write different pools / workspaces.
+ *
+ * Data layout (all little-endian)
+ *   G = 32 (key-group tokens and value-group channels), P = page tokens,
+ *   D = head_dim, row = D/4 bytes (2-bit codes, channel 4k+i in bits
+ *   [2i,2i+1] of byte k).
+ *   Pool of one stored cell: H x num_pages head-blocks, head-major: head h
+ *   of physical page p starts at byte (h*num_pages + p) * HB.
+ *   4-bit head-block: K_hi[P rows] K_lo[P rows] V_hi[P rows] V_lo[P rows]
+ *                     Vmeta[P][D/G]{fp16 scale, fp16 zero}
+ *                     Kmeta[max(1,P/G) slots]{fp16 scale[D], fp16 zero[D]}
+ *   2-bit head-block: K[P rows] V[P rows] Vmeta Kmeta.
+ *   Key group g (tokens 32g..32g+31) keeps its metadata in the page holding
+ *   token 32g, slot (32g mod P)/32.  A 4-bit code c is stored as
+ *   hi = c >> 2 in the *_hi plane and lo = c & 3 in the *_lo plane.
+ */
+#ifndef LOOPKV_H
+#define LOOPKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOOPKV_ABI_VERSION 1
+
+enum {
+  LOOPKV_OK = 0,
+  LOOPKV_NOOP_REUSE = 1,   /* append on a reuse cell: nothing to store     */
+  LOOPKV_E_INVAL = -1,     /* bad argument                                  */
+  LOOPKV_E_PLAN = -2,      /* malformed or invalid plan blob                */
+  LOOPKV_E_CAPACITY = -3,  /* workspace / staging / pool too small          */
+  LOOPKV_E_HIP = -4        /* HIP runtime error (message has HIP's text)    */
+};
+
+enum { LOOPKV_CELL_Q4 = 0, LOOPKV_CELL_Q2 = 1, LOOPKV_CELL_REUSE = 2 };
+
+typedef struct loopkv_plan loopkv_plan; /* opaque, host, immutable */
+
+/* ABI version compiled into the library (compare with LOOPKV_ABI_VERSION). */
+int loopkv_abi_version(void);
+
+/* Thread-local text of the last error ("" if none).  Valid until the next
+ * call on the same thread. */
+const char* loopkv_last_error(void);
+
+/*
+ * loopkv_plan_load -- parse the per-cell plan.
+ * Source: LoopKV abstract -- the offline profile picks 4-bit, 2-bit or
+ * final-loop reuse for every (loop, layer) cell; a threshold tau per cell
+ * decides where the low bits are fetched.
+ * blob (host, nbytes): "LKVP", u32 version = 1, i32 R, L, H, D, G, P, then
+ *   R*L records {u8 kind, u8 pad[3], f32 tau} in [loop][layer] order.
+ * Accepted: R >= 1, L >= 1, 1 <= H <= 1024, D in {64, 128}, G == 32,
+ *   P in {16, 32, 64}; kind in {Q4, Q2, REUSE}; REUSE only in loops
+ *   0..R-2; tau >= 0 or +inf, never NaN.
+ * out: receives a new plan (free with loopkv_plan_free).
+ * Errors: LOOPKV_E_INVAL for NULL pointers, LOOPKV_E_PLAN otherwise.
+ */
+int loopkv_plan_load(const void* blob, size_t nbytes, loopkv_plan** out);
+void loopkv_plan_free(loopkv_plan* plan);
+
+/* dims[6] <- R, L, H, D, G, P.  Errors: LOOPKV_E_INVAL. */
+int loopkv_plan_dims(const loopkv_plan* plan, int32_t dims[6]);
+
+/* Cell (loop, layer): its kind, its tau and the loop of the cell whose
+ * cache it reads (R-1 for REUSE, else `loop`).  Any output may be NULL. */
+int loopkv_cell_info(const loopkv_plan* plan, int loop, int layer,
+                     int* kind, float* tau, int* src_loop);
+
+/* Bytes of one head-block (HB) of the cell's pool; 0 for REUSE or bad args. */
+size_t loopkv_head_block_bytes(const loopkv_plan* plan, int loop, int layer);
+
+/* Bytes of a pool of num_pages pages (H * num_pages * HB); 0 for REUSE. */
+size_t loopkv_pool_bytes(const loopkv_plan* plan, int loop, int layer,
+                         int64_t num_pages);
+
+/* Bytes of the key staging buffer of a stored cell for max_slots
+ * sequences: max_slots * H * 32 * D bf16 (raw keys of each sequence's open,
+ * incomplete key group).  0 for REUSE. */
+size_t loopkv_staging_bytes(const loopkv_plan* plan, int loop, int layer,
+                            int32_t max_slots);
+
+/* Device workspace bytes loopkv_decode needs for `batch` sequences of at
+ * most max_seq_len tokens (any cell of the plan, any split count). */
+size_t loopkv_decode_workspace_bytes(const loopkv_plan* plan, int32_t batch,
+                                     int32_t max_seq_len);
+
+/* Memory of one cell; an array of R*L of these is indexed [loop*L + layer].
+ * REUSE cells may leave everything NULL / 0. */
+typedef struct {
+  void* pool;          /* device, loopkv_pool_bytes(num_pages) bytes         */
+  void* staging;       /* device, loopkv_staging_bytes(max_slots) bytes      */
+  int64_t num_pages;   /* pages in this pool (shared page numbering)         */
+  int32_t max_slots;   /* staging slots                                      */
+  int32_t reserved;
+} loopkv_cell_mem;
+
+/* One batch of sequences.  Every cell uses the same page mapping. */
+typedef struct {
+  int32_t batch;                /* number of sequences B >= 0                */
+  int32_t max_pages;            /* row stride of block_tables                */
+  const int32_t* seq_lens;      /* device [B]: append = length BEFORE the
+                                   append; decode = tokens attended          */
+  const int32_t* slots;         /* device [B] staging slot per sequence, or
+                                   NULL for slot = sequence index            */
+  const int32_t* block_tables;  /* device [B][max_pages]: logical page ->
+                                   physical page (0 <= p < num_pages)        */
+  int32_t max_seq_len;          /* host upper bound of the lengths involved
+                                   (decode: attended; append: after append)  */
+  int32_t reserved;
+} loopkv_batch;
+
+/*
+ * loopkv_append -- quantize and store n_new new tokens of every sequence in
+ * cell (loop, layer).
+ * Source: LoopKV abstract (cells stored at 4 or 2 bits; 4-bit values kept
+ * as separately readable high and low bit planes).
+ * k_bf16, v_bf16: device [B][n_new][H][D] bfloat16 (raw keys and values of
+ *   tokens seq_lens[b] .. seq_lens[b]+n_new-1).
+ * Effects: value rows and metadata of the new tokens; key codes and key
+ *   metadata of every key group the new tokens touch (the open group of a
+ *   sequence is re-quantized over all its tokens, read back from staging);
+ *   staging then holds the raw keys of each sequence's open group.
+ *   Pages for all tokens < seq_lens[b] + n_new must be mapped.  Values must
+ *   be finite with |x| <= 32768.
+ * Returns LOOPKV_NOOP_REUSE (nothing launched) for a reuse cell.
+ * Errors: LOOPKV_E_INVAL (bad cell, NULL pool/staging, n_new < 1,
+ *   batch > max_slots when slots == NULL, max_pages * P < max_seq_len),
+ *   LOOPKV_E_HIP.
+ */
+int loopkv_append(const loopkv_plan* plan, const loopkv_cell_mem* cells,
+                  int loop, int layer, const loopkv_batch* batch,
+                  int32_t n_new, const void* k_bf16, const void* v_bf16,
+                  void* stream);
+
+typedef struct {
+  float sm_scale;              /* score = sm_scale * q . k                    */
+  int32_t num_splits;          /* splits per (sequence, head); 0 = automatic  */
+  void* workspace;             /* device, loopkv_decode_workspace_bytes       */
+  size_t workspace_bytes;
+  uint32_t* mask_bits;         /* optional device [B][H][ceil(max_seq_len/32)]:
+                                  bit t of a (b, h) row = low plane of token t
+                                  fetched (all ones up to T for tau = 0)      */
+  unsigned long long* counters;/* optional device [2], accumulated with
+                                  atomics: [0] flagged token-heads,
+                                  [1] low-plane bytes read                    */
+} loopkv_decode_opts;
+
+/*
+ * loopkv_decode -- one decode step of cell (loop, layer) for every sequence.
+ * Source: LoopKV abstract -- the cell reads its source cache (itself, or
+ * the final loop's cell of its layer for REUSE), dequantizes keys at the
+ * source's precision, forms softmax weights from its own query, reads the
+ * high plane of every value and fetches the low plane only of tokens whose
+ * own weight p_t >= tau of the calling cell.  An unfetched 4-bit value is
+ * reconstructed at its bucket centre (4*hi + 3/2)*s + z.
+ * q_bf16: device [B][H][D] bfloat16.  out: device [B][H][D] float32.
+ * A sequence of length 0 produces zeros.
+ * Errors: LOOPKV_E_INVAL (bad cell, NULL pointers, num_splits < 0,
+ *   max_pages * P < max_seq_len), LOOPKV_E_CAPACITY (workspace too small),
+ *   LOOPKV_E_HIP.
+ */
+int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells,
+                  int loop, int layer, const loopkv_batch* batch,
+                  const void* q_bf16, float* out,
+                  const loopkv_decode_opts* opts, void* stream);
+
+/*
+ * Measurement hook (not an operation of the method; used by benchmarks to
+ * time kernels live).  While enabled, every kernel launch this library makes
+ * is bracketed by a pair of HIP events recorded on the launch's own stream.
+ * loopkv_profile_collect waits for the recorded events of one kernel class
+ * (LOOPKV_KERNEL_*), returns the number of launches and their summed
+ * duration in milliseconds, and clears that class.  Enabling/disabling is
+ * process-wide; the events are created by the library on first use and
+ * reused.  Errors: LOOPKV_E_INVAL (bad class or NULL output), LOOPKV_E_HIP.
+ */
+enum { LOOPKV_KERNEL_SPLIT = 0, LOOPKV_KERNEL_MERGE = 1, LOOPKV_KERNEL_APPEND = 2 };
+int loopkv_profile_enable(int on);
+int loopkv_profile_collect(int kernel_class, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOOPKV_H */

@@ -1,0 +1,440 @@
+// abi.hip -- host side of the C ABI declared in include/loopkv.h: plan
+// parsing and validation, argument checks, split selection and launches.
+//
+// Source of the plan semantics: "LoopKV: Loop-Aware KV Cache Compression for
+// Serving Looped Transformers", abstract (概要) -- one offline decision per
+// (loop, layer) cell among 4-bit storage, 2-bit storage and reuse of the
+// final loop's KV of that layer, with decode-time low-bit fetches decided
+// by the cell's own attention weights (threshold tau per cell).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "layout.hpp"
+#include "loopkv.h"
+
+struct loopkv_plan {
+  int32_t R, L, H, D, G, P;
+  std::vector<uint8_t> kind;   // [R*L]
+  std::vector<float> tau;      // [R*L]
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return LOOPKV_E_HIP;
+}
+
+bool debug_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("LOOPKV_DEBUG");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+int32_t rd_i32(const uint8_t* p) {
+  int32_t v;
+  std::memcpy(&v, p, 4);
+  return v;
+}
+
+bool cell_ok(const loopkv_plan* plan, int loop, int layer) {
+  return plan && loop >= 0 && loop < plan->R && layer >= 0 && layer < plan->L;
+}
+
+int cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= static_cast<int>(cache.size())) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Split plan for `pairs` (sequence, head) pairs of at most t_max tokens.
+struct Splits {
+  int S, len;
+};
+
+Splits choose_splits(int64_t pairs, int t_max, int requested) {
+  const int64_t tm = std::max<int64_t>(t_max, 1);
+  int64_t s0;
+  if (requested > 0) {
+    s0 = requested;
+  } else {
+    // aim for several resident waves per compute unit
+    const int64_t target = static_cast<int64_t>(cu_count()) * 8;
+    s0 = std::max<int64_t>(1, (target + pairs - 1) / std::max<int64_t>(pairs, 1));
+    // keep splits long enough to amortize the per-split epilogue
+    s0 = std::min<int64_t>(s0, std::max<int64_t>(1, tm / 512));
+  }
+  s0 = std::max<int64_t>(s0, (tm + lkv::kMaxSplitLen - 1) / lkv::kMaxSplitLen);
+  int64_t len = round_up((tm + s0 - 1) / s0, lkv::kTile);
+  len = std::min<int64_t>(len, lkv::kMaxSplitLen);
+  const int64_t S = (tm + len - 1) / len;
+  return {static_cast<int>(S), static_cast<int>(len)};
+}
+
+struct WorkspacePlan {
+  size_t partials, counts, cand, total;
+};
+
+WorkspacePlan workspace_plan(int64_t batch, int64_t H, int64_t D, int64_t t_max) {
+  const int64_t tm = std::max<int64_t>(t_max, 1);
+  const int64_t s_cap = std::min<int64_t>(lkv::kMaxSplits, round_up(tm, lkv::kTile) / lkv::kTile);
+  const int64_t cand_per_pair = round_up(tm, lkv::kTile) + std::min<int64_t>(lkv::kMaxSplitLen, round_up(tm, lkv::kTile));
+  WorkspacePlan w;
+  w.partials = static_cast<size_t>(round_up(batch * H * s_cap * (D + lkv::kPartialPad) * 4, 256));
+  w.counts = static_cast<size_t>(round_up(batch * H * s_cap * 4, 256));
+  w.cand = static_cast<size_t>(round_up(batch * H * cand_per_pair * 8, 256));
+  w.total = w.partials + w.counts + w.cand;
+  return w;
+}
+
+// LOOPKV_DEBUG=1: copy lengths / tables / slots to the host and check them.
+int debug_check(const loopkv_batch* bt, int P, int64_t num_pages, int extra, int max_slots,
+                hipStream_t stream) {
+  const int B = bt->batch;
+  std::vector<int32_t> lens(B), table(static_cast<size_t>(B) * bt->max_pages), slots;
+  hipError_t e = hipMemcpyAsync(lens.data(), bt->seq_lens, B * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(table.data(), bt->block_tables, table.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess && bt->slots && max_slots > 0) {
+    slots.resize(B);
+    e = hipMemcpyAsync(slots.data(), bt->slots, B * 4, hipMemcpyDeviceToHost, stream);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail_hip(e, "debug copy of batch metadata");
+  for (int b = 0; b < B; ++b) {
+    const int64_t T = static_cast<int64_t>(lens[b]) + extra;
+    if (lens[b] < 0 || T > bt->max_seq_len)
+      return fail(LOOPKV_E_INVAL, "seq_lens[" + std::to_string(b) + "] out of range");
+    const int64_t pages = (T + P - 1) / P;
+    for (int64_t p = 0; p < pages; ++p) {
+      const int32_t v = table[static_cast<size_t>(b) * bt->max_pages + p];
+      if (v < 0 || v >= num_pages)
+        return fail(LOOPKV_E_INVAL, "block_tables[" + std::to_string(b) + "][" + std::to_string(p) +
+                                        "] out of range");
+    }
+    if (!slots.empty() && (slots[b] < 0 || slots[b] >= max_slots))
+      return fail(LOOPKV_E_INVAL, "slots[" + std::to_string(b) + "] out of range");
+  }
+  return LOOPKV_OK;
+}
+
+// ---- measurement hook: event pairs around launches, per kernel class ----
+struct ProfClass {
+  std::vector<hipEvent_t> ev;  // start, stop, start, stop, ...
+  size_t used = 0;             // events recorded since the last collect
+};
+
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  ProfClass cls[lkv::kClasses];
+};
+
+Profiler& profiler() {
+  static Profiler p;
+  return p;
+}
+
+}  // namespace
+
+namespace lkv {
+
+void prof_mark(int c, int phase, hipStream_t stream) {
+  Profiler& p = profiler();
+  std::lock_guard<std::mutex> lock(p.mu);
+  if (!p.on) return;
+  ProfClass& pc = p.cls[c];
+  // a stop mark pairs with the start recorded just before it
+  if (phase == 1 && pc.used % 2 == 0) return;
+  if (phase == 0 && pc.used % 2 == 1) pc.used -= 1;  // unmatched start: reuse its slot
+  if (pc.used == pc.ev.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    pc.ev.push_back(e);
+  }
+  if (hipEventRecord(pc.ev[pc.used], stream) == hipSuccess) pc.used += 1;
+}
+
+}  // namespace lkv
+
+extern "C" {
+
+int loopkv_profile_enable(int on) {
+  Profiler& p = profiler();
+  std::lock_guard<std::mutex> lock(p.mu);
+  p.on = on != 0;
+  return LOOPKV_OK;
+}
+
+int loopkv_profile_collect(int kernel_class, int64_t* launches, double* total_ms) {
+  if (kernel_class < 0 || kernel_class >= lkv::kClasses || !launches || !total_ms)
+    return fail(LOOPKV_E_INVAL, "profile_collect: bad kernel class or NULL output");
+  Profiler& p = profiler();
+  std::lock_guard<std::mutex> lock(p.mu);
+  ProfClass& pc = p.cls[kernel_class];
+  const size_t pairs = pc.used / 2;
+  double ms = 0.0;
+  for (size_t i = 0; i < pairs; ++i) {
+    hipError_t e = hipEventSynchronize(pc.ev[2 * i + 1]);
+    float t = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, pc.ev[2 * i], pc.ev[2 * i + 1]);
+    if (e != hipSuccess) {
+      pc.used = 0;
+      return fail_hip(e, "profile_collect");
+    }
+    ms += t;
+  }
+  pc.used = 0;
+  *launches = static_cast<int64_t>(pairs);
+  *total_ms = ms;
+  return LOOPKV_OK;
+}
+
+int loopkv_abi_version(void) { return LOOPKV_ABI_VERSION; }
+
+const char* loopkv_last_error(void) { return g_err.c_str(); }
+
+int loopkv_plan_load(const void* blob, size_t nbytes, loopkv_plan** out) {
+  if (!out) return fail(LOOPKV_E_INVAL, "plan_load: out is NULL");
+  *out = nullptr;
+  if (!blob) return fail(LOOPKV_E_INVAL, "plan_load: blob is NULL");
+  const uint8_t* p = static_cast<const uint8_t*>(blob);
+  if (nbytes < 32) return fail(LOOPKV_E_PLAN, "plan_load: blob shorter than its 32-byte header");
+  if (std::memcmp(p, "LKVP", 4) != 0) return fail(LOOPKV_E_PLAN, "plan_load: bad magic (want LKVP)");
+  uint32_t version;
+  std::memcpy(&version, p + 4, 4);
+  if (version != 1) return fail(LOOPKV_E_PLAN, "plan_load: unsupported version " + std::to_string(version));
+  const int32_t R = rd_i32(p + 8), L = rd_i32(p + 12), H = rd_i32(p + 16), D = rd_i32(p + 20),
+                G = rd_i32(p + 24), P = rd_i32(p + 28);
+  if (R < 1 || R > 4096 || L < 1 || L > 4096)
+    return fail(LOOPKV_E_PLAN, "plan_load: loops and layers must be in [1, 4096]");
+  if (H < 1 || H > 1024) return fail(LOOPKV_E_PLAN, "plan_load: heads must be in [1, 1024]");
+  if (D != 64 && D != 128) return fail(LOOPKV_E_PLAN, "plan_load: head_dim must be 64 or 128");
+  if (G != lkv::kGroup) return fail(LOOPKV_E_PLAN, "plan_load: group size must be 32");
+  if (P != 16 && P != 32 && P != 64) return fail(LOOPKV_E_PLAN, "plan_load: page size must be 16, 32 or 64");
+  const size_t cells = static_cast<size_t>(R) * L;
+  if (nbytes != 32 + 8 * cells)
+    return fail(LOOPKV_E_PLAN, "plan_load: blob size " + std::to_string(nbytes) + " != 32 + 8*R*L = " +
+                                   std::to_string(32 + 8 * cells));
+  loopkv_plan* plan = new (std::nothrow) loopkv_plan;
+  if (!plan) return fail(LOOPKV_E_PLAN, "plan_load: out of host memory");
+  plan->R = R; plan->L = L; plan->H = H; plan->D = D; plan->G = G; plan->P = P;
+  plan->kind.resize(cells);
+  plan->tau.resize(cells);
+  for (size_t c = 0; c < cells; ++c) {
+    const uint8_t* rec = p + 32 + 8 * c;
+    const int loop = static_cast<int>(c / L), layer = static_cast<int>(c % L);
+    float tau;
+    std::memcpy(&tau, rec + 4, 4);
+    const std::string where = "cell (" + std::to_string(loop) + ", " + std::to_string(layer) + ")";
+    if (rec[0] > lkv::kKindReuse) {
+      delete plan;
+      return fail(LOOPKV_E_PLAN, "plan_load: " + where + " has unknown kind " + std::to_string(rec[0]));
+    }
+    if (rec[0] == lkv::kKindReuse && loop == R - 1) {
+      delete plan;
+      return fail(LOOPKV_E_PLAN, "plan_load: " + where + " is in the final loop and cannot reuse it");
+    }
+    if (std::isnan(tau) || tau < 0.0f) {
+      delete plan;
+      return fail(LOOPKV_E_PLAN, "plan_load: " + where + " has tau that is NaN or negative");
+    }
+    plan->kind[c] = rec[0];
+    plan->tau[c] = tau;
+  }
+  *out = plan;
+  return LOOPKV_OK;
+}
+
+void loopkv_plan_free(loopkv_plan* plan) { delete plan; }
+
+int loopkv_plan_dims(const loopkv_plan* plan, int32_t dims[6]) {
+  if (!plan || !dims) return fail(LOOPKV_E_INVAL, "plan_dims: NULL argument");
+  dims[0] = plan->R; dims[1] = plan->L; dims[2] = plan->H;
+  dims[3] = plan->D; dims[4] = plan->G; dims[5] = plan->P;
+  return LOOPKV_OK;
+}
+
+int loopkv_cell_info(const loopkv_plan* plan, int loop, int layer, int* kind, float* tau, int* src_loop) {
+  if (!cell_ok(plan, loop, layer)) return fail(LOOPKV_E_INVAL, "cell_info: no such cell");
+  const size_t c = static_cast<size_t>(loop) * plan->L + layer;
+  if (kind) *kind = plan->kind[c];
+  if (tau) *tau = plan->tau[c];
+  if (src_loop) *src_loop = plan->kind[c] == lkv::kKindReuse ? plan->R - 1 : loop;
+  return LOOPKV_OK;
+}
+
+size_t loopkv_head_block_bytes(const loopkv_plan* plan, int loop, int layer) {
+  if (!cell_ok(plan, loop, layer)) return 0;
+  const int k = plan->kind[static_cast<size_t>(loop) * plan->L + layer];
+  if (k == lkv::kKindReuse) return 0;
+  return static_cast<size_t>(lkv::make_layout(k, plan->P, plan->D).HB);
+}
+
+size_t loopkv_pool_bytes(const loopkv_plan* plan, int loop, int layer, int64_t num_pages) {
+  if (num_pages < 0) return 0;
+  return loopkv_head_block_bytes(plan, loop, layer) * static_cast<size_t>(plan ? plan->H : 0) *
+         static_cast<size_t>(num_pages);
+}
+
+size_t loopkv_staging_bytes(const loopkv_plan* plan, int loop, int layer, int32_t max_slots) {
+  if (!cell_ok(plan, loop, layer) || max_slots < 0) return 0;
+  if (plan->kind[static_cast<size_t>(loop) * plan->L + layer] == lkv::kKindReuse) return 0;
+  return static_cast<size_t>(max_slots) * plan->H * lkv::kGroup * plan->D * 2;
+}
+
+size_t loopkv_decode_workspace_bytes(const loopkv_plan* plan, int32_t batch, int32_t max_seq_len) {
+  if (!plan || batch < 0 || max_seq_len < 0) return 0;
+  return workspace_plan(batch, plan->H, plan->D, max_seq_len).total;
+}
+
+int loopkv_append(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loop, int layer,
+                  const loopkv_batch* batch, int32_t n_new, const void* k_bf16, const void* v_bf16,
+                  void* stream) {
+  if (!plan || !cells || !batch) return fail(LOOPKV_E_INVAL, "append: NULL plan, cells or batch");
+  if (!cell_ok(plan, loop, layer)) return fail(LOOPKV_E_INVAL, "append: no such cell");
+  const size_t c = static_cast<size_t>(loop) * plan->L + layer;
+  if (plan->kind[c] == lkv::kKindReuse) {
+    g_err.clear();
+    return LOOPKV_NOOP_REUSE;
+  }
+  const loopkv_cell_mem& mem = cells[c];
+  if (!mem.pool || !mem.staging) return fail(LOOPKV_E_INVAL, "append: cell pool or staging is NULL");
+  if (mem.num_pages < 1) return fail(LOOPKV_E_INVAL, "append: cell has no pages");
+  if (batch->batch < 0) return fail(LOOPKV_E_INVAL, "append: negative batch");
+  if (n_new < 1) return fail(LOOPKV_E_INVAL, "append: n_new must be >= 1");
+  if (batch->batch == 0) return LOOPKV_OK;
+  if (!k_bf16 || !v_bf16) return fail(LOOPKV_E_INVAL, "append: NULL key or value input");
+  if (!batch->seq_lens || !batch->block_tables)
+    return fail(LOOPKV_E_INVAL, "append: NULL seq_lens or block_tables");
+  if (batch->max_pages < 1) return fail(LOOPKV_E_INVAL, "append: max_pages must be >= 1");
+  if (static_cast<int64_t>(batch->max_pages) * plan->P < batch->max_seq_len)
+    return fail(LOOPKV_E_INVAL, "append: max_pages * page_size < max_seq_len");
+  if (batch->max_seq_len < n_new) return fail(LOOPKV_E_INVAL, "append: max_seq_len < n_new");
+  if (!batch->slots && batch->batch > mem.max_slots)
+    return fail(LOOPKV_E_CAPACITY, "append: batch exceeds the cell's staging slots");
+  if (mem.max_slots < 1) return fail(LOOPKV_E_CAPACITY, "append: cell has no staging slots");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_enabled()) {
+    const int rc = debug_check(batch, plan->P, mem.num_pages, n_new, mem.max_slots, s);
+    if (rc != LOOPKV_OK) return rc;
+  }
+  lkv::AppendArgs a{};
+  a.pool = static_cast<uint8_t*>(mem.pool);
+  a.staging = static_cast<uint16_t*>(mem.staging);
+  a.seq_lens = batch->seq_lens;
+  a.slots = batch->slots;
+  a.block_tables = batch->block_tables;
+  a.k_in = static_cast<const uint16_t*>(k_bf16);
+  a.v_in = static_cast<const uint16_t*>(v_bf16);
+  a.num_pages = mem.num_pages;
+  a.H = plan->H;
+  a.max_pages = batch->max_pages;
+  a.n_new = n_new;
+  a.lay = lkv::make_layout(plan->kind[c], plan->P, plan->D);
+  const hipError_t e = lkv::launch_append(a, batch->batch, s);
+  if (e != hipSuccess) return fail_hip(e, "append: kernel launch");
+  g_err.clear();
+  return LOOPKV_OK;
+}
+
+int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loop, int layer,
+                  const loopkv_batch* batch, const void* q_bf16, float* out,
+                  const loopkv_decode_opts* opts, void* stream) {
+  if (!plan || !cells || !batch || !opts) return fail(LOOPKV_E_INVAL, "decode: NULL plan, cells, batch or opts");
+  if (!cell_ok(plan, loop, layer)) return fail(LOOPKV_E_INVAL, "decode: no such cell");
+  const size_t c = static_cast<size_t>(loop) * plan->L + layer;
+  const int src_loop = plan->kind[c] == lkv::kKindReuse ? plan->R - 1 : loop;
+  const size_t sc = static_cast<size_t>(src_loop) * plan->L + layer;
+  const int src_kind = plan->kind[sc];
+  const float tau = plan->tau[c];
+  const loopkv_cell_mem& mem = cells[sc];
+  if (!mem.pool) return fail(LOOPKV_E_INVAL, "decode: source cell pool is NULL");
+  if (mem.num_pages < 1) return fail(LOOPKV_E_INVAL, "decode: source cell has no pages");
+  if (batch->batch < 0) return fail(LOOPKV_E_INVAL, "decode: negative batch");
+  if (opts->num_splits < 0) return fail(LOOPKV_E_INVAL, "decode: num_splits must be >= 0");
+  if (batch->max_seq_len < 0) return fail(LOOPKV_E_INVAL, "decode: negative max_seq_len");
+  if (batch->batch == 0) return LOOPKV_OK;
+  if (!q_bf16 || !out) return fail(LOOPKV_E_INVAL, "decode: NULL query or output");
+  if (!batch->seq_lens || !batch->block_tables)
+    return fail(LOOPKV_E_INVAL, "decode: NULL seq_lens or block_tables");
+  if (batch->max_pages < 1) return fail(LOOPKV_E_INVAL, "decode: max_pages must be >= 1");
+  if (static_cast<int64_t>(batch->max_pages) * plan->P < batch->max_seq_len)
+    return fail(LOOPKV_E_INVAL, "decode: max_pages * page_size < max_seq_len");
+  const WorkspacePlan wp = workspace_plan(batch->batch, plan->H, plan->D, batch->max_seq_len);
+  if (!opts->workspace || opts->workspace_bytes < wp.total)
+    return fail(LOOPKV_E_CAPACITY, "decode: workspace smaller than loopkv_decode_workspace_bytes (" +
+                                       std::to_string(wp.total) + " bytes)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_enabled()) {
+    const int rc = debug_check(batch, plan->P, mem.num_pages, 0, 0, s);
+    if (rc != LOOPKV_OK) return rc;
+  }
+  const int64_t pairs = static_cast<int64_t>(batch->batch) * plan->H;
+  const Splits sp = choose_splits(pairs, batch->max_seq_len, opts->num_splits);
+  if (sp.S > lkv::kMaxSplits) return fail(LOOPKV_E_INVAL, "decode: max_seq_len needs too many splits");
+
+  int mode = lkv::kModePlain;
+  if (src_kind == lkv::kKindQ4) {
+    if (tau == 0.0f) mode = lkv::kModeDense;
+    else if (std::isfinite(tau)) mode = lkv::kModeSparse;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(opts->workspace);
+  lkv::DecodeArgs a{};
+  a.pool = static_cast<const uint8_t*>(mem.pool);
+  a.seq_lens = batch->seq_lens;
+  a.block_tables = batch->block_tables;
+  a.q = static_cast<const uint16_t*>(q_bf16);
+  a.out = out;
+  a.partials = reinterpret_cast<float*>(ws);
+  a.cand_count = reinterpret_cast<int32_t*>(ws + wp.partials);
+  a.cand = reinterpret_cast<int2*>(ws + wp.partials + wp.counts);
+  a.mask_bits = opts->mask_bits;
+  a.counters = opts->counters;
+  a.num_pages = mem.num_pages;
+  a.H = plan->H;
+  a.max_pages = batch->max_pages;
+  a.S = sp.S;
+  a.split_len = sp.len;
+  a.mask_words = (batch->max_seq_len + 31) / 32;
+  a.sm_scale = opts->sm_scale;
+  a.log_tau = (mode == lkv::kModeSparse) ? std::log(tau) : 0.0f;
+  a.lay = lkv::make_layout(src_kind, plan->P, plan->D);
+  const hipError_t e = lkv::launch_decode(a, batch->batch, mode, s);
+  if (e != hipSuccess) return fail_hip(e, "decode: kernel launch");
+  g_err.clear();
+  return LOOPKV_OK;
+}
+
+}  // extern "C"

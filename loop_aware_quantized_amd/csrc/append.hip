@@ -1,0 +1,212 @@
+// append.hip -- quantize/pack kernel: appends new tokens of a stored cell
+// into its bit-plane paged pool.
+//
+// Source: "LoopKV: Loop-Aware KV Cache Compression for Serving Looped
+// Transformers", abstract (概要) -- cells are stored at 4 or 2 bits, and a
+// 4-bit value is split so that its high two bits can be read without its
+// low two bits.  Group layout (keys per channel over 32 tokens, values per
+// token over 32 channels, fp16 scale and zero point) after the KIVI entry
+// of the related-papers list on the fugumt LoopVQ page.
+//
+// One 64-lane wave handles one (sequence, head, key group touched by the
+// new tokens).  A key group that already holds tokens is re-quantized over
+// all of them: their raw keys come back from the staging buffer, so the
+// stored cache is a pure function of the token sequence.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace lkv {
+namespace {
+
+template <int D, int KIND>
+__global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
+  constexpr float kLevels = (KIND == kKindQ4) ? 15.0f : 3.0f;
+  constexpr int kWords = D / 16;   // 16 two-bit fields per 32-bit word
+  constexpr int kNJ = D / kGroup;  // value channel groups
+  __shared__ float raw[kGroup][D];
+  __shared__ float ks[D], kz[D];
+
+  const int lane = threadIdx.x;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int H = a.H;
+  const CellLayout L = a.lay;
+  const int T0 = a.seq_lens[b];
+  const int T1 = T0 + a.n_new;
+  const int g0 = T0 / kGroup;
+  const int g = g0 + static_cast<int>(blockIdx.x);
+  const int gs = g * kGroup;
+  if (gs >= T1) return;
+  const int ge = min(gs + kGroup, T1);
+  const int n = ge - gs;
+  const int slot = a.slots ? a.slots[b] : b;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_pages;
+  uint8_t* hbase = a.pool + static_cast<int64_t>(h) * a.num_pages * L.HB;
+  uint16_t* stg = a.staging + (static_cast<int64_t>(slot) * H + h) * kGroup * D;
+
+  // raw keys of the group: staged (old) tokens, then new tokens
+  for (int idx = lane; idx < n * (D / 2); idx += 64) {
+    const int i = idx / (D / 2), pr = idx % (D / 2);
+    const int t = gs + i;
+    uint32_t w;
+    if (t < T0) {
+      w = reinterpret_cast<const uint32_t*>(stg)[i * (D / 2) + pr];
+    } else {
+      const int64_t src = ((static_cast<int64_t>(b) * a.n_new + (t - T0)) * H + h) * (D / 2) + pr;
+      w = reinterpret_cast<const uint32_t*>(a.k_in)[src];
+    }
+    raw[i][2 * pr] = bf16_to_f32(static_cast<uint16_t>(w & 0xffffu));
+    raw[i][2 * pr + 1] = bf16_to_f32(static_cast<uint16_t>(w >> 16));
+  }
+  __syncthreads();
+
+  // key metadata: one channel per lane
+  {
+    const int lp = gs / L.P;
+    const int kslot = (gs % L.P) / kGroup;
+    uint16_t* km = reinterpret_cast<uint16_t*>(
+        hbase + static_cast<int64_t>(bt[lp]) * L.HB + L.off_kmeta + kslot * 4 * D);
+    for (int d = lane; d < D; d += 64) {
+      float mn = raw[0][d], mx = mn;
+      for (int i = 1; i < n; ++i) {
+        mn = fminf(mn, raw[i][d]);
+        mx = fmaxf(mx, raw[i][d]);
+      }
+      const QParams q = qparams(mn, mx, kLevels);
+      ks[d] = q.s;
+      kz[d] = q.z;
+      km[d] = q.sbits;
+      km[D + d] = q.zbits;
+    }
+  }
+  __syncthreads();
+
+  // key codes of every token of the group: one (token, 16-channel word) per task
+  for (int idx = lane; idx < n * kWords; idx += 64) {
+    const int i = idx / kWords, k = idx % kWords;
+    const int t = gs + i;
+    uint32_t whi = 0, wlo = 0;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int d = 16 * k + c;
+      QParams q;
+      q.s = ks[d];
+      q.z = kz[d];
+      const uint32_t code = qcode(raw[i][d], q, kLevels);
+      if (KIND == kKindQ4) {
+        whi |= (code >> 2) << (2 * c);
+        wlo |= (code & 3u) << (2 * c);
+      } else {
+        whi |= code << (2 * c);
+      }
+    }
+    const int r = t % L.P;
+    uint8_t* blk = hbase + static_cast<int64_t>(bt[t / L.P]) * L.HB;
+    reinterpret_cast<uint32_t*>(blk + L.off_khi + r * L.row)[k] = whi;
+    if (KIND == kKindQ4) reinterpret_cast<uint32_t*>(blk + L.off_klo + r * L.row)[k] = wlo;
+  }
+
+  // value codes and metadata of the new tokens: one (token, channel group) per task
+  const int first_new = max(gs, T0);
+  const int nv = ge - first_new;
+  for (int idx = lane; idx < nv * kNJ; idx += 64) {
+    const int i = idx / kNJ, j = idx % kNJ;
+    const int t = first_new + i;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.v_in) +
+        (((static_cast<int64_t>(b) * a.n_new + (t - T0)) * H + h) * D + kGroup * j) / 2;
+    float x[kGroup];
+#pragma unroll
+    for (int e = 0; e < kGroup / 2; ++e) {
+      const uint32_t w = src[e];
+      x[2 * e] = bf16_to_f32(static_cast<uint16_t>(w & 0xffffu));
+      x[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(w >> 16));
+    }
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int c = 1; c < kGroup; ++c) {
+      mn = fminf(mn, x[c]);
+      mx = fmaxf(mx, x[c]);
+    }
+    const QParams q = qparams(mn, mx, kLevels);
+    uint32_t hi[2] = {0, 0}, lo[2] = {0, 0};
+#pragma unroll
+    for (int c = 0; c < kGroup; ++c) {
+      const uint32_t code = qcode(x[c], q, kLevels);
+      if (KIND == kKindQ4) {
+        hi[c / 16] |= (code >> 2) << (2 * (c % 16));
+        lo[c / 16] |= (code & 3u) << (2 * (c % 16));
+      } else {
+        hi[c / 16] |= code << (2 * (c % 16));
+      }
+    }
+    const int r = t % L.P;
+    uint8_t* blk = hbase + static_cast<int64_t>(bt[t / L.P]) * L.HB;
+    *reinterpret_cast<uint2*>(blk + L.off_vhi + r * L.row + 8 * j) = make_uint2(hi[0], hi[1]);
+    if (KIND == kKindQ4)
+      *reinterpret_cast<uint2*>(blk + L.off_vlo + r * L.row + 8 * j) = make_uint2(lo[0], lo[1]);
+    reinterpret_cast<uint32_t*>(blk + L.off_vmeta)[r * kNJ + j] =
+        static_cast<uint32_t>(q.sbits) | (static_cast<uint32_t>(q.zbits) << 16);
+  }
+
+  // staging: keep the raw keys of the sequence's open group.  Done here only
+  // when this group is both the first and the last one touched (the usual
+  // one-token append); otherwise append_staging_kernel runs afterwards, so
+  // no wave overwrites staging rows another wave still reads.
+  if (g == g0 && ge == T1 && (T1 % kGroup) != 0) {
+    for (int idx = lane; idx < (ge - first_new) * (D / 2); idx += 64) {
+      const int i = idx / (D / 2), pr = idx % (D / 2);
+      const int t = first_new + i;
+      const int64_t src = ((static_cast<int64_t>(b) * a.n_new + (t - T0)) * H + h) * (D / 2) + pr;
+      reinterpret_cast<uint32_t*>(stg)[(t - gs) * (D / 2) + pr] =
+          reinterpret_cast<const uint32_t*>(a.k_in)[src];
+    }
+  }
+}
+
+// Staging refresh for appends that span several key groups: copy the raw
+// keys of the (new) open group into the sequence's staging slot.
+template <int D>
+__global__ __launch_bounds__(64) void append_staging_kernel(AppendArgs a) {
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int H = a.H;
+  const int T0 = a.seq_lens[b];
+  const int T1 = T0 + a.n_new;
+  if (T1 % kGroup == 0) return;
+  const int gl = (T1 - 1) / kGroup;
+  if (gl == T0 / kGroup) return;  // handled inside append_pack_kernel
+  const int gs = gl * kGroup;     // > T0: every token of the open group is new
+  const int slot = a.slots ? a.slots[b] : b;
+  uint32_t* stg = reinterpret_cast<uint32_t*>(a.staging + (static_cast<int64_t>(slot) * H + h) * kGroup * D);
+  for (int idx = lane; idx < (T1 - gs) * (D / 2); idx += 64) {
+    const int i = idx / (D / 2), pr = idx % (D / 2);
+    const int t = gs + i;
+    const int64_t src = ((static_cast<int64_t>(b) * a.n_new + (t - T0)) * H + h) * (D / 2) + pr;
+    stg[i * (D / 2) + pr] = reinterpret_cast<const uint32_t*>(a.k_in)[src];
+  }
+}
+
+template <int D, int KIND>
+hipError_t launch_typed(const AppendArgs& a, int batch, hipStream_t stream) {
+  const int groups = (a.n_new + kGroup - 1) / kGroup + 1;
+  prof_mark(kClassAppend, 0, stream);
+  hipLaunchKernelGGL((append_pack_kernel<D, KIND>), dim3(groups, a.H, batch), dim3(64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && a.n_new > 1) {
+    hipLaunchKernelGGL((append_staging_kernel<D>), dim3(a.H, batch), dim3(64), 0, stream, a);
+    e = hipGetLastError();
+  }
+  prof_mark(kClassAppend, 1, stream);
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t stream) {
+  const bool q4 = a.lay.kind == kKindQ4;
+  if (a.lay.D == 128) return q4 ? launch_typed<128, kKindQ4>(a, batch, stream)
+                                : launch_typed<128, kKindQ2>(a, batch, stream);
+  return q4 ? launch_typed<64, kKindQ4>(a, batch, stream)
+            : launch_typed<64, kKindQ2>(a, batch, stream);
+}
+
+}  // namespace lkv

@@ -1,0 +1,95 @@
+// device.hpp -- small device helpers shared by the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace lkv {
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+__device__ __forceinline__ uint16_t f16_bits_rne(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// Next fp16 bit pattern towards -inf / +inf (finite or infinite input).
+__device__ __forceinline__ uint16_t f16_next_down(uint16_t h) {
+  if ((h & 0x7fffu) == 0) return 0x8001u;          // +-0 -> -min subnormal
+  return (h & 0x8000u) ? static_cast<uint16_t>(h + 1) : static_cast<uint16_t>(h - 1);
+}
+__device__ __forceinline__ uint16_t f16_next_up(uint16_t h) {
+  if ((h & 0x7fffu) == 0) return 0x0001u;
+  return (h & 0x8000u) ? static_cast<uint16_t>(h - 1) : static_cast<uint16_t>(h + 1);
+}
+
+// Largest fp16 <= x and smallest fp16 >= x (directed conversions built on
+// the hardware's round-to-nearest-even conversion).
+__device__ __forceinline__ uint16_t f16_round_down_bits(float x) {
+  uint16_t h = f16_bits_rne(x);
+  if (f16_to_f32(h) > x) h = f16_next_down(h);
+  return h;
+}
+__device__ __forceinline__ uint16_t f16_round_up_bits(float x) {
+  uint16_t h = f16_bits_rne(x);
+  if (f16_to_f32(h) < x) h = f16_next_up(h);
+  return h;
+}
+
+// Quantizer parameters of one group: zero = fp16 round-down of the minimum,
+// scale = fp16 round-up of fp32((max - zero) / levels).
+struct QParams {
+  uint16_t zbits, sbits;
+  float z, s;
+};
+
+__device__ __forceinline__ QParams qparams(float mn, float mx, float levels) {
+  QParams q;
+  q.zbits = f16_round_down_bits(mn);
+  q.z = f16_to_f32(q.zbits);
+  const float r = mx - q.z;          // IEEE fp32 subtraction
+  const float s32 = r / levels;      // IEEE fp32 division (no fast-math)
+  q.sbits = f16_round_up_bits(s32);
+  q.s = f16_to_f32(q.sbits);
+  return q;
+}
+
+// code = clamp(rint_even(fp32(fp32(x - z) / s)), 0, levels); 0 when s == 0.
+__device__ __forceinline__ uint32_t qcode(float x, const QParams& q, float levels) {
+  if (!(q.s > 0.0f)) return 0u;
+  const float t = (x - q.z) / q.s;
+  float c = __builtin_rintf(t);
+  c = fminf(fmaxf(c, 0.0f), levels);
+  return static_cast<uint32_t>(c);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over the 32 lanes of each half-wave.
+__device__ __forceinline__ float half_wave_sum(float v) {
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float byte_f(uint32_t w, int k) {
+  return static_cast<float>((w >> (8 * k)) & 0xffu);
+}
+
+}  // namespace lkv

@@ -1,0 +1,64 @@
+// kernels.hpp -- argument blocks and launchers of the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "layout.hpp"
+
+namespace lkv {
+
+struct AppendArgs {
+  uint8_t* pool;
+  uint16_t* staging;            // [slots][H][32][D] bf16
+  const int32_t* seq_lens;      // length before the append
+  const int32_t* slots;         // may be null
+  const int32_t* block_tables;
+  const uint16_t* k_in;         // [B][n_new][H][D] bf16
+  const uint16_t* v_in;
+  int64_t num_pages;
+  int32_t H, max_pages, n_new;
+  CellLayout lay;
+};
+
+// Maximum split length whose scores fit the split kernel's LDS buffer.
+constexpr int kMaxSplitLen = 4096;
+// Maximum number of splits per (sequence, head).
+constexpr int kMaxSplits = 2048;
+constexpr int kTile = 64;            // tokens per wave iteration
+constexpr int kPartialPad = 4;       // floats before o[] in a partial record
+
+struct DecodeArgs {
+  const uint8_t* pool;
+  const int32_t* seq_lens;
+  const int32_t* block_tables;
+  const uint16_t* q;                 // [B][H][D] bf16
+  float* out;                        // [B][H][D]
+  float* partials;                   // [B][H][S][D + kPartialPad]
+  int2* cand;                        // [B][H][S][split_len] (token, score bits)
+  int32_t* cand_count;               // [B][H][S]
+  uint32_t* mask_bits;               // optional [B][H][mask_words]
+  unsigned long long* counters;      // optional [2]
+  int64_t num_pages;
+  int32_t H, max_pages, S, split_len, mask_words;
+  float sm_scale;
+  float log_tau;                     // ln(tau) for the candidate / flag test
+  CellLayout lay;
+};
+
+// mode of a decode launch
+enum DecodeMode : int {
+  kModePlain = 0,      // 2-bit source, or 4-bit with tau = +inf: no low plane
+  kModeSparse = 1,     // 4-bit, 0 < tau < inf: candidates + flagged gather
+  kModeDense = 2,      // 4-bit, tau = 0: every low plane read in the split pass
+};
+
+// Measurement hook: brackets one launch of kernel class `cls` with events
+// when profiling is enabled (no-op otherwise).  phase 0 = before, 1 = after.
+enum { kClassSplit = 0, kClassMerge = 1, kClassAppend = 2, kClasses = 3 };
+void prof_mark(int cls, int phase, hipStream_t stream);
+
+hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int batch, int mode, hipStream_t stream);
+
+}  // namespace lkv

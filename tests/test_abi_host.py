@@ -1,0 +1,169 @@
+"""C-ABI library on the host (no GPU): it loads, exports every function that
+include/loopkv.h declares, parses and validates plans, answers size queries,
+and rejects bad host-visible arguments before launching anything.
+"""
+import ctypes
+import math
+import os
+import re
+import struct
+
+import pytest
+
+from loop_aware_quantized_amd import abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "loopkv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(abi.LIB_PATH),
+                                reason="libloopkv.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(loopkv_[a-z_0-9]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert "loopkv_decode" in names and "loopkv_append" in names and "loopkv_plan_load" in names
+    handle = ctypes.CDLL(abi.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), n
+    assert set(names) == set(abi._SIGNATURES), "binding and header disagree"
+
+
+def test_abi_version():
+    assert abi.lib().loopkv_abi_version() == abi.ABI_VERSION == 1
+
+
+def _blob(R=2, L=2, H=2, D=64, P=16, kinds=None, taus=None, G=32):
+    kinds = kinds or [[0, 2], [1, 0]]
+    taus = taus or [[0.02] * L for _ in range(R)]
+    return abi.plan_blob(R, L, H, D, P, kinds, taus, G=G)
+
+
+def test_plan_load_and_queries():
+    p = abi.Plan(_blob())
+    assert (p.R, p.L, p.H, p.D, p.G, p.P) == (2, 2, 2, 64, 32, 16)
+    assert p.cell_info(0, 1) == (2, pytest.approx(0.02), 1)   # reuse -> final loop
+    assert p.cell_info(1, 0)[0] == 1 and p.cell_info(1, 0)[2] == 1
+    # head-block of a 4-bit cell, P=16, D=64: 4 planes * 16 rows * 16 B + 16*2*4 + 64*4
+    assert p.head_block_bytes(0, 0) == 4 * 256 + 128 + 256
+    assert p.head_block_bytes(1, 0) == 2 * 256 + 128 + 256
+    assert p.head_block_bytes(0, 1) == 0
+    assert p.pool_bytes(0, 0, 10) == 10 * 2 * 1408
+    assert p.staging_bytes(0, 0, 3) == 3 * 2 * 32 * 64 * 2
+    assert p.staging_bytes(0, 1, 3) == 0
+    assert p.decode_workspace_bytes(4, 1000) > 0
+    p.close()
+
+
+def _load_rc(blob):
+    h = ctypes.c_void_p()
+    buf = ctypes.create_string_buffer(blob, len(blob))
+    rc = abi.lib().loopkv_plan_load(ctypes.cast(buf, ctypes.c_void_p), len(blob), ctypes.byref(h))
+    if rc == 0:
+        abi.lib().loopkv_plan_free(h)
+    return rc, abi.last_error()
+
+
+@pytest.mark.parametrize("mutate, text", [
+    (lambda b: b"XXXX" + b[4:], "magic"),
+    (lambda b: b[:4] + struct.pack("<I", 2) + b[8:], "version"),
+    (lambda b: b[:20], "shorter"),
+    (lambda b: b + b"\0" * 8, "blob size"),
+])
+def test_plan_rejects_malformed(mutate, text):
+    rc, msg = _load_rc(mutate(_blob()))
+    assert rc == abi.E_PLAN and text in msg
+
+
+@pytest.mark.parametrize("kw, text", [
+    (dict(kinds=[[0, 0], [2, 0]]), "final loop"),
+    (dict(kinds=[[0, 3], [1, 0]]), "unknown kind"),
+    (dict(taus=[[math.nan, 0.1], [0.1, 0.1]]), "NaN or negative"),
+    (dict(taus=[[-0.1, 0.1], [0.1, 0.1]]), "NaN or negative"),
+    (dict(D=96), "head_dim"),
+    (dict(P=24), "page size"),
+    (dict(G=16), "group size"),
+])
+def test_plan_rejects_invalid(kw, text):
+    rc, msg = _load_rc(_blob(**kw))
+    assert rc == abi.E_PLAN and text in msg
+
+
+def test_plan_accepts_inf_and_zero_tau():
+    rc, _ = _load_rc(_blob(taus=[[0.0, math.inf], [math.inf, 0.0]]))
+    assert rc == 0
+
+
+def test_null_arguments():
+    assert abi.lib().loopkv_plan_load(None, 0, None) == abi.E_INVAL
+    assert abi.lib().loopkv_plan_dims(None, None) == abi.E_INVAL
+    assert abi.lib().loopkv_head_block_bytes(None, 0, 0) == 0
+
+
+class _FakeTensor:
+    """Stands in for a device tensor: only its address is used by the binding."""
+
+    def __init__(self, addr, shape=(1,), nbytes=16):
+        self.addr, self.shape, self._n = addr, shape, nbytes
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 1
+
+
+def test_append_and_decode_reject_bad_host_arguments():
+    p = abi.Plan(_blob())
+    cells = abi.cell_array(p, {(0, 0): (_FakeTensor(0x1000), _FakeTensor(0x2000), 4, 1),
+                                (1, 0): (_FakeTensor(0x3000), _FakeTensor(0x4000), 4, 1),
+                                (1, 1): (_FakeTensor(0x5000), _FakeTensor(0x6000), 4, 1)})
+    lens = _FakeTensor(0x7000, shape=(1,))
+    table = _FakeTensor(0x8000, shape=(1, 4))
+    b = abi.make_batch(lens, table, max_seq_len=64)
+    k = _FakeTensor(0x9000)
+    lib = abi.lib()
+
+    def app(loop, layer, n_new, batch=b, kk=k):
+        return lib.loopkv_append(p.handle, ctypes.cast(cells, ctypes.c_void_p), loop, layer,
+                                 ctypes.byref(batch), n_new, kk and kk.data_ptr(),
+                                 kk and kk.data_ptr(), None)
+
+    assert app(0, 1, 1) == abi.NOOP_REUSE            # reuse cell stores nothing
+    assert app(5, 0, 1) == abi.E_INVAL                # no such cell
+    assert app(0, 0, 0) == abi.E_INVAL                # n_new < 1
+    assert app(0, 0, 1, kk=None) == abi.E_INVAL       # NULL inputs
+    big = abi.make_batch(lens, table, max_seq_len=65)  # 4 pages * 16 < 65
+    assert app(0, 0, 1, batch=big) == abi.E_INVAL
+    assert "max_pages" in abi.last_error()
+    two = abi.make_batch(lens, table, max_seq_len=64, batch=2)  # 2 sequences, 1 staging slot
+    assert app(0, 0, 1, batch=two) == abi.E_CAPACITY
+
+    out = _FakeTensor(0xA000)
+    small_ws = _FakeTensor(0xB000, nbytes=16)
+
+    def dec(loop, layer, opts, batch=b):
+        return lib.loopkv_decode(p.handle, ctypes.cast(cells, ctypes.c_void_p), loop, layer,
+                                 ctypes.byref(batch), k.data_ptr(), out.data_ptr(),
+                                 ctypes.byref(opts), None)
+
+    assert dec(0, 0, abi.make_opts(small_ws)) == abi.E_CAPACITY
+    assert "workspace" in abi.last_error()
+    assert dec(0, 0, abi.make_opts(small_ws, num_splits=-1)) == abi.E_INVAL
+    assert dec(7, 0, abi.make_opts(small_ws)) == abi.E_INVAL
+    assert dec(0, 0, abi.make_opts(small_ws), batch=big) == abi.E_INVAL
+    # a reuse cell resolves to the final loop's pool of its layer: (1, 1)
+    empty = abi.cell_array(p, {(0, 0): (_FakeTensor(0x1000), _FakeTensor(0x2000), 4, 1)})
+    rc = lib.loopkv_decode(p.handle, ctypes.cast(empty, ctypes.c_void_p), 0, 1, ctypes.byref(b),
+                           k.data_ptr(), out.data_ptr(), ctypes.byref(abi.make_opts(small_ws)), None)
+    assert rc == abi.E_INVAL and "source cell pool" in abi.last_error()
+    p.close()

@@ -1,0 +1,206 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Sizes here span several 64-token tiles, every page size, both head dims,
+ragged tails, empty sequences, all three decode modes (tau = 0, finite tau,
+tau = +inf), 2-bit cells and reuse cells of both source kinds.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from loop_aware_quantized_amd import abi
+from loop_aware_quantized_amd import inputs as wl
+from loop_aware_quantized_amd import runner
+from oracle import attention as oa
+from parity_util import check_pool, compare_decode, say, tau_str
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+Q4, Q2, RU = wl.KIND_Q4, wl.KIND_Q2, wl.KIND_REUSE
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _decode(st, r, l, num_splits=0, q=None):
+    w = st.w
+    if q is None:
+        q = wl.cell_query(w, st.cell_index(r, l), DEV)[1]
+    out = torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=DEV)
+    mask = st.new_mask()
+    cnt = torch.zeros(2, dtype=torch.int64, device=DEV)
+    st.decode(r, l, q, out, num_splits=num_splits, mask=mask, counters=cnt)
+    torch.cuda.synchronize()
+    return q, out, mask, cnt
+
+
+def _all_cells(st, kept, seqs, num_splits=0):
+    stats = {}
+    for r in range(st.w.loops):
+        for l in range(st.w.layers):
+            q, out, mask, cnt = _decode(st, r, l, num_splits)
+            src = oa.resolve_source(st.kinds, r, l)
+            s = compare_decode(st, r, l, q, out, mask, kept[src], seqs)
+            stats[(r, l)] = s
+            say(f"  cell ({r},{l}) src {src} kind {st.kinds[src]} tau {tau_str(st.taus[r, l])}: "
+                f"rel err {s['rel']:.2e} flagged {s['flagged']} band {s['band']}")
+    return stats
+
+
+def test_tiny_workload_end_to_end():
+    w = wl.WORKLOADS["tiny"]
+    st = runner.CacheState(w, DEV)
+    kept = st.prefill({c: set(range(w.batch)) for c in st.stored})
+    torch.cuda.synchronize()
+    for (r, l) in st.stored:
+        for b in range(w.batch):
+            check_pool(st, r, l, b, *kept[(r, l)][b])
+    stats = _all_cells(st, kept, range(w.batch))
+    assert sum(s["flagged"] for s in stats.values()) > 0, "tiny workload should flag heavy tokens"
+
+
+MIXED_KINDS = [[Q4, Q2, RU, RU], [Q4, Q4, Q2, Q4]]
+MIXED_TAUS = [[0.01, 0.02, 0.0, 0.005], [0.0, math.inf, 0.01, 0.03]]
+MIXED_LENS = [1, 63, 64, 65, 700, 2049]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("P", [16, 32, 64])
+def test_mixed_plan_ragged(D, P):
+    say(f"mixed plan D={D} P={P}")
+    w = wl.Workload(f"mixed-{D}-{P}", 100 + D + P, batch=len(MIXED_LENS), loops=2, layers=4,
+                    heads=3, head_dim=D, page=P, ctx=max(MIXED_LENS), heavy_frac=0.01,
+                    shuffle_pages=(P == 16))
+    st = runner.CacheState(w, DEV, MIXED_KINDS, MIXED_TAUS, lengths=MIXED_LENS)
+    kept = st.prefill({c: set(range(w.batch)) for c in st.stored})
+    torch.cuda.synchronize()
+    for (r, l) in st.stored:
+        for b in range(w.batch):
+            check_pool(st, r, l, b, *kept[(r, l)][b])
+    _all_cells(st, kept, range(w.batch))
+
+
+def test_empty_and_short_sequences():
+    w = wl.Workload("short", 130, batch=4, loops=1, layers=2, heads=2, head_dim=128, page=16,
+                    ctx=300, heavy_frac=0.02)
+    st = runner.CacheState(w, DEV, [[Q4, Q2]], [[0.01, 0.01]], lengths=[0, 5, 300, 32])
+    kept = st.prefill({c: set(range(w.batch)) for c in st.stored})
+    torch.cuda.synchronize()
+    for l in range(2):
+        q, out, mask, _ = _decode(st, 0, l)
+        assert torch.all(out[0] == 0)
+        compare_decode(st, 0, l, q, out, mask, kept[(0, l)], range(w.batch))
+
+
+def test_split_counts_and_page_shuffle():
+    """num_splits 1 / 3 / auto all match the oracle; shuffled page tables give
+    bit-identical outputs to contiguous ones."""
+    kinds, taus = [[Q4, Q2]], [[0.005, 0.005]]
+    lens = [3000, 4096, 1500]
+    outs = {}
+    for shuffle in (False, True):
+        w = wl.Workload("splits", 140, batch=3, loops=1, layers=2, heads=4, head_dim=128, page=16,
+                        ctx=4096, heavy_frac=0.01, shuffle_pages=shuffle)
+        st = runner.CacheState(w, DEV, kinds, taus, lengths=lens)
+        kept = st.prefill({c: set(range(3)) for c in st.stored})
+        for l in range(2):
+            for ns in (1, 3, 0):
+                q, out, mask, _ = _decode(st, 0, l, num_splits=ns)
+                compare_decode(st, 0, l, q, out, mask, kept[(0, l)], range(3))
+                outs[(shuffle, l, ns)] = (out.cpu().numpy(), mask.cpu().numpy())
+    for l in range(2):
+        for ns in (1, 3, 0):
+            a, b = outs[(False, l, ns)], outs[(True, l, ns)]
+            assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
+            assert np.array_equal(a[1], b[1])
+
+
+def test_decode_is_deterministic():
+    w = wl.Workload("determ", 150, batch=2, loops=1, layers=1, heads=4, head_dim=128, page=32,
+                    ctx=5000, heavy_frac=0.01)
+    st = runner.CacheState(w, DEV, [[Q4]], [[0.002]])
+    st.prefill()
+    res = [_decode(st, 0, 0) for _ in range(3)]
+    for q, out, mask, cnt in res[1:]:
+        assert torch.equal(out.view(torch.int32), res[0][1].view(torch.int32))
+        assert torch.equal(mask, res[0][2])
+        assert torch.equal(cnt, res[0][3])
+
+
+def _append_all(st, K, V, schedule):
+    """Append K/V [B][T][H][D] following schedule [(t0, t1), ...] (same for all sequences)."""
+    for (r, l) in st.stored:
+        for (t0, t1) in schedule:
+            lens = torch.full((st.w.batch,), t0, dtype=torch.int32, device=DEV)
+            st.append(r, l, K[(r, l)][:, t0:t1].contiguous(), V[(r, l)][:, t0:t1].contiguous(), lens)
+
+
+def test_append_token_by_token_equals_bulk():
+    """The cache is a pure function of the sequence: one-token appends, a
+    multi-group append and a single bulk append give identical bytes, equal
+    to the oracle's packing."""
+    T = 100
+    w = wl.Workload("append", 160, batch=3, loops=1, layers=2, heads=2, head_dim=128, page=16,
+                    ctx=T, heavy_frac=0.01)
+    kinds, taus = [[Q4, Q2]], [[0.01, 0.01]]
+    a = runner.CacheState(w, DEV, kinds, taus, lengths=[T] * 3)
+    b = runner.CacheState(w, DEV, kinds, taus, lengths=[T] * 3)
+    K, V = {}, {}
+    for (r, l) in a.stored:
+        K[(r, l)], V[(r, l)] = wl.cell_kv(w, a.cell_index(r, l), T, DEV)
+    _append_all(a, K, V, [(0, T)])
+    sched = [(0, 37)] + [(t, t + 1) for t in range(37, 60)] + [(60, T)]
+    _append_all(b, K, V, sched)
+    torch.cuda.synchronize()
+    for (r, l) in a.stored:
+        for s in range(3):
+            kb, vb = wl.bf16_bits(K[(r, l)][s]), wl.bf16_bits(V[(r, l)][s])
+            check_pool(a, r, l, s, kb, vb)
+            check_pool(b, r, l, s, kb, vb)
+
+
+def test_append_ragged_lengths_and_staging():
+    """Appends from different starting lengths per sequence, including ones
+    that cross key groups, then decode over the result."""
+    w = wl.Workload("append-ragged", 170, batch=4, loops=1, layers=2, heads=2, head_dim=64,
+                    page=32, ctx=160, heavy_frac=0.02)
+    kinds, taus = [[Q4, Q2]], [[0.0, 0.01]]
+    start = np.array([0, 31, 33, 64], np.int32)
+    steps = [1, 2, 45, 1]
+    final = start + sum(steps)
+    st = runner.CacheState(w, DEV, kinds, taus, lengths=final)
+    T = int(final.max())
+    kept = {}
+    for (r, l) in st.stored:
+        K, V = wl.cell_kv(w, st.cell_index(r, l), T, DEV)
+        # per-sequence starting contents: sequence b holds its first start[b] tokens
+        for bi in range(w.batch):
+            n0 = int(start[bi])
+            if n0:
+                lens = torch.zeros(1, dtype=torch.int32, device=DEV)
+                batch = abi.make_batch(lens, st.block_tables[bi:bi + 1], st.max_seq_len,
+                                       slots=st.slots[bi:bi + 1])
+                abi.loopkv_append(st.plan, st.cells, r, l, batch, n0, K[bi:bi + 1, :n0].contiguous(),
+                                  V[bi:bi + 1, :n0].contiguous())
+        cur = start.copy()
+        for n in steps:
+            lens = torch.from_numpy(cur).to(DEV)
+            idx = torch.from_numpy((cur[:, None] + np.arange(n)[None, :]).astype(np.int64)).to(DEV)
+            kk = torch.stack([K[bi, idx[bi]] for bi in range(w.batch)])
+            vv = torch.stack([V[bi, idx[bi]] for bi in range(w.batch)])
+            st.append(r, l, kk, vv, lens)
+            cur = cur + n
+        kept[(r, l)] = {bi: (wl.bf16_bits(K[bi]), wl.bf16_bits(V[bi])) for bi in range(w.batch)}
+    torch.cuda.synchronize()
+    for (r, l) in st.stored:
+        for bi in range(w.batch):
+            check_pool(st, r, l, bi, *kept[(r, l)][bi])
+    for l in range(2):
+        q, out, mask, _ = _decode(st, 0, l)
+        compare_decode(st, 0, l, q, out, mask, kept[(0, l)], range(w.batch))
