@@ -84,7 +84,11 @@ def compare_decode(state, r, l, q, out, mask, host_kv, seqs, lens=None):
     band_total = flagged = 0
     for b in seqs:
         T = int(lens[b])
-        k_bits, v_bits = host_kv[b]
+        if T == 0:
+            empty = np.zeros((0, state.w.heads, state.w.head_dim), np.uint16)
+            k_bits, v_bits = empty, empty
+        else:
+            k_bits, v_bits = host_kv[b]
         cache = oc.build_cell_cache(k_bits[:T], v_bits[:T], kind)
         res = oa.decode(cache, q_bits[b], tau)
         if T > 0 and mask_h is not None:
