@@ -124,6 +124,8 @@ size_t loopkv_decode_workspace_bytes(const loopkv_plan* plan, int32_t batch,
 
 /* Memory of one cell; an array of R*L of these is indexed [loop*L + layer].
  * REUSE cells may leave everything NULL / 0. */
+/* Limit: one head's region of a pool, num_pages * head-block bytes, must
+ * stay below 4 GiB (decode addresses it with 32-bit offsets). */
 typedef struct {
   void* pool;          /* device, loopkv_pool_bytes(num_pages) bytes         */
   void* staging;       /* device, loopkv_staging_bytes(max_slots) bytes      */

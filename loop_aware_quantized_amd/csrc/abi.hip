@@ -90,7 +90,7 @@ Splits choose_splits(int64_t pairs, int t_max, int requested) {
     s0 = requested;
   } else {
     // aim for several resident waves per compute unit
-    const int64_t target = static_cast<int64_t>(cu_count()) * 8;
+    const int64_t target = static_cast<int64_t>(cu_count()) * 12;
     s0 = std::max<int64_t>(1, (target + pairs - 1) / std::max<int64_t>(pairs, 1));
     // keep splits long enough to amortize the per-split epilogue
     s0 = std::min<int64_t>(s0, std::max<int64_t>(1, tm / 512));
@@ -332,6 +332,8 @@ int loopkv_append(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
   const loopkv_cell_mem& mem = cells[c];
   if (!mem.pool || !mem.staging) return fail(LOOPKV_E_INVAL, "append: cell pool or staging is NULL");
   if (mem.num_pages < 1) return fail(LOOPKV_E_INVAL, "append: cell has no pages");
+  if (static_cast<uint64_t>(mem.num_pages) * lkv::make_layout(plan->kind[c], plan->P, plan->D).HB > 0xFFFFFFFFull)
+    return fail(LOOPKV_E_INVAL, "append: one head's pool region (num_pages * head-block bytes) exceeds 4 GiB");
   if (batch->batch < 0) return fail(LOOPKV_E_INVAL, "append: negative batch");
   if (n_new < 1) return fail(LOOPKV_E_INVAL, "append: n_new must be >= 1");
   if (batch->batch == 0) return LOOPKV_OK;
@@ -382,6 +384,8 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
   const loopkv_cell_mem& mem = cells[sc];
   if (!mem.pool) return fail(LOOPKV_E_INVAL, "decode: source cell pool is NULL");
   if (mem.num_pages < 1) return fail(LOOPKV_E_INVAL, "decode: source cell has no pages");
+  if (static_cast<uint64_t>(mem.num_pages) * lkv::make_layout(src_kind, plan->P, plan->D).HB > 0xFFFFFFFFull)
+    return fail(LOOPKV_E_INVAL, "decode: one head's pool region (num_pages * head-block bytes) exceeds 4 GiB");
   if (batch->batch < 0) return fail(LOOPKV_E_INVAL, "decode: negative batch");
   if (opts->num_splits < 0) return fail(LOOPKV_E_INVAL, "decode: num_splits must be >= 0");
   if (batch->max_seq_len < 0) return fail(LOOPKV_E_INVAL, "decode: negative max_seq_len");

@@ -45,28 +45,80 @@ __device__ __forceinline__ uint32_t field(uint32_t w, int i) {
   return w & (0x03030303u << (2 * i));
 }
 
-// 4-bit codes from a high and a low plane word, position i of each byte:
-// i < 3: (4*hi + lo) * 4^i;  i == 3: (4*hi + lo) * 16.
-__device__ __forceinline__ uint32_t combine(uint32_t hw, uint32_t lw, int i) {
-  const uint32_t m = 0x03030303u << (2 * i);
-  return i < 3 ? (((hw & m) << 2) | (lw & m)) : ((hw & m) | ((lw & m) >> 2));
+// Converts the four bytes of w, each holding an integer n < 16, to floats.
+// An fp8 (e4m3) byte below 16 is a subnormal or lies in the first normal
+// binade, whose spacing is the same, so it converts to exactly n * unit with
+// unit a power of two fixed by the format (read back at run time).
+__device__ __forceinline__ void cvt_bytes(uint32_t w, float* f) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = hi[0]; f[3] = hi[1];
 }
+
+// Unpacks one 32-bit word of 16 two-bit fields (channel 4b + i in bits
+// [8b + 2i, 8b + 2i + 1]) into 16 floats in "position" order p = 4i + b.
+// Positions with odd i come out multiplied by 4 (field left in bits 2-3 of
+// its byte); multipliers compensate with plain_factor.
+__device__ __forceinline__ void unpack_plain(uint32_t w, float* f) {
+  const uint32_t u = w >> 4;
+  cvt_bytes(w & 0x03030303u, f);
+  cvt_bytes(w & 0x0C0C0C0Cu, f + 4);
+  cvt_bytes(u & 0x03030303u, f + 8);
+  cvt_bytes(u & 0x0C0C0C0Cu, f + 12);
+}
+
+// Unpacks a high-plane word and a low-plane word into 16 four-bit codes
+// 4*hi + lo as floats, in the same position order p = 4i + b.
+__device__ __forceinline__ void unpack_combined(uint32_t h, uint32_t l, float* f) {
+  // even fields (i = 0, 2) as nibbles: lo bits stay, hi bits move up by 2
+  const uint32_t e = ((h << 2) & 0xCCCCCCCCu) | (l & 0x33333333u);
+  // odd fields (i = 1, 3): hi bits stay, lo bits move down by 2
+  const uint32_t o = (h & 0xCCCCCCCCu) | ((l >> 2) & 0x33333333u);
+  cvt_bytes(e & 0x0F0F0F0Fu, f);
+  cvt_bytes(o & 0x0F0F0F0Fu, f + 4);
+  cvt_bytes((e >> 4) & 0x0F0F0F0Fu, f + 8);
+  cvt_bytes((o >> 4) & 0x0F0F0F0Fu, f + 12);
+}
+
+// channel (within a 16-channel word) of position p, and its multiplier for
+// plain 2-bit fields (odd i arrive times 4)
+__host__ __device__ constexpr int pos_channel(int p) { return 4 * (p % 4) + p / 4; }
+__host__ __device__ constexpr int channel_pos(int m) { return 4 * (m % 4) + m / 4; }
+__device__ __forceinline__ constexpr float plain_factor(int p) { return ((p / 4) & 1) ? 0.25f : 1.0f; }
+
+// Everything one 64-token tile reads from HBM, held in registers so the next
+// tile's loads are in flight while the current tile computes.
+template <int D, bool kQ4, bool kDense>
+struct TileData {
+  static constexpr int kNJ = D / kGroup;
+  static constexpr int kSubs = kTile / (64 / kNJ);
+  uint4 kh[D / 64];                 // this lane's token: key row (high plane)
+  uint4 kl[kQ4 ? D / 64 : 1];       // key row, low plane
+  uint2 vh[kSubs];                  // value rows: 32 channels of one token each
+  uint2 vl[kDense ? kSubs : 1];
+  uint32_t vm[kSubs];               // value (scale, zero) of that token/group
+  uint32_t ks[D / 64], kz[D / 64];  // key-group scale / zero of this lane's channels
+};
 
 template <int D, int KIND, int MODE>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   constexpr int kNJ = D / kGroup;       // value channel groups
   constexpr int kSlots = 64 / kNJ;      // tokens per value step
+  constexpr int kSubs = kTile / kSlots; // value steps per tile
   constexpr int kWords = D / 16;        // 32-bit words per row
   constexpr int kCPL = D / 32;          // channels per lane in the meta step
   constexpr bool kQ4 = KIND == kKindQ4;
   constexpr bool kSparse = MODE == kModeSparse;
   constexpr bool kDense = MODE == kModeDense;
+  constexpr bool kKeyComb = kQ4;            // keys: 4-bit codes from two planes
+  constexpr bool kValComb = kQ4 && kDense;  // values: both planes only when tau = 0
+  using Tile = TileData<D, kQ4, kDense>;
 
   __shared__ float qs[D];
-  __shared__ float qk[2][D];
+  __shared__ float qk[2][D];                 // per-channel key multipliers, position order
   __shared__ float bias_s[2];
   __shared__ float ptile[kTile];
-  __shared__ float sc[kSparse ? kMaxSplitLen : 1];
+  __shared__ uint32_t pgoff[kMaxSplitLen / 16];
 
   const int lane = threadIdx.x;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -87,43 +139,112 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     return;
   }
 
+  // page size is a power of two; the split starts on a page boundary.
+  // pgoff[i]: byte offset, inside this head's pool region, of the split's
+  // i-th page (physical page * head-block bytes).
+  const int lgP = __builtin_ctz(static_cast<unsigned>(L.P));
+  const int pmask = L.P - 1;
+  {
+    const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_pages + (start >> lgP);
+    const int np = ((end - start) + pmask) >> lgP;
+    for (int i = lane; i < np; i += 64)
+      pgoff[i] = static_cast<uint32_t>(bt[i]) * static_cast<uint32_t>(L.HB);
+  }
   for (int d = lane; d < D; d += 64) qs[d] = bf16_to_f32(a.q[pair * D + d]) * a.sm_scale;
   __syncthreads();
 
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_pages;
-  const uint8_t* hbase = a.pool + static_cast<int64_t>(h) * a.num_pages * L.HB;
+  // this head's pool region as a raw buffer: 32-bit offsets, and loads past
+  // the region return zero instead of faulting
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.pool + static_cast<int64_t>(h) * a.num_pages * L.HB), static_cast<short>(0),
+      static_cast<int>(static_cast<uint32_t>(a.num_pages * L.HB)), 0x00020000);
   const int vj = lane % kNJ, vslot = lane / kNJ;
+  const int gsel = lane >> 5;
+  const int d0 = (lane & 31) * kCPL;
+  const int last = end - 1;
+  const float unit = __builtin_amdgcn_cvt_pk_f32_fp8(1, false)[0];
+  const float inv_unit = 1.0f / unit;
+
+  // byte offset of token t's row inside its page's head-block
+  auto row_off = [&](int t) -> uint32_t {
+    return pgoff[(t - start) >> lgP] + static_cast<uint32_t>((t & pmask) * (D / 4));
+  };
+  auto ld128 = [&](uint32_t off) -> uint4 {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  };
+  auto ld64 = [&](uint32_t off) -> uint2 {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, 0);
+    return make_uint2(v[0], v[1]);
+  };
+  auto ld32 = [&](uint32_t off) -> uint32_t { return __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0); };
+
+  // Issue every load of the tile starting at t0.  Token indices are clamped
+  // to the split, so every address is valid; clamped lanes are masked later.
+  auto fetch = [&](Tile& td, int t0) {
+    {
+      const uint32_t ro = row_off(min(t0 + lane, last));
+#pragma unroll
+      for (int v = 0; v < D / 64; ++v) td.kh[v] = ld128(ro + L.off_khi + 16 * v);
+      if (kQ4) {
+#pragma unroll
+        for (int v = 0; v < D / 64; ++v) td.kl[v] = ld128(ro + L.off_klo + 16 * v);
+      }
+    }
+#pragma unroll
+    for (int sub = 0; sub < kSubs; ++sub) {
+      const int tt = min(t0 + sub * kSlots + vslot, last);
+      const uint32_t ro = row_off(tt);
+      td.vh[sub] = ld64(ro + L.off_vhi + 8 * vj);
+      if (kDense) td.vl[sub] = ld64(ro + L.off_vlo + 8 * vj);
+      td.vm[sub] = ld32(pgoff[(tt - start) >> lgP] + L.off_vmeta + ((tt & pmask) * kNJ + vj) * 4);
+    }
+    {
+      int gtok = t0 + kGroup * gsel;
+      if (gtok > last) gtok = t0;     // second group absent: read the first (unused)
+      const uint32_t mo = pgoff[(gtok - start) >> lgP] + L.off_kmeta +
+                          ((gtok & pmask) / kGroup) * 4 * D + 2 * d0;
+      if (D == 128) {
+        const uint2 s2 = ld64(mo), z2 = ld64(mo + 2 * D);
+        td.ks[0] = s2.x; td.ks[D / 64 - 1] = s2.y;
+        td.kz[0] = z2.x; td.kz[D / 64 - 1] = z2.y;
+      } else {
+        td.ks[0] = ld32(mo);
+        td.kz[0] = ld32(mo + 2 * D);
+      }
+    }
+  };
 
   float m = -INFINITY, lsum = 0.0f, zs = 0.0f;
   float acc[32];
 #pragma unroll
   for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
+  int2* cand_list = a.cand + (pair * a.S + split) * a.split_len;
+  int n_cand = 0;
 
+  Tile cur;
+  fetch(cur, start);
   for (int t0 = start; t0 < end; t0 += kTile) {
+    Tile nxt;
+    fetch(nxt, t0 + kTile <= last ? t0 + kTile : t0);
+
     // --- key metadata of the tile's two key groups -> per-channel multipliers
     {
-      const int gsel = lane >> 5;
-      const int gtok = t0 + kGroup * gsel;
-      const int d0 = (lane & 31) * kCPL;
+      const bool gvalid = t0 + kGroup * gsel <= last;
       float bpart = 0.0f;
-      if (gtok < end) {
-        const int lp = gtok / L.P, ksl = (gtok % L.P) / kGroup;
-        const uint16_t* km = reinterpret_cast<const uint16_t*>(
-            hbase + static_cast<int64_t>(bt[lp]) * L.HB + L.off_kmeta + ksl * 4 * D);
 #pragma unroll
-        for (int c = 0; c < kCPL; ++c) {
-          const int d = d0 + c;
-          const float s = f16_to_f32(km[d]);
-          const float z = f16_to_f32(km[D + d]);
-          const float qv = qs[d];
-          bpart = fmaf(qv, z, bpart);
-          qk[gsel][d] = qv * s * posf<kQ4>(d & 3);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < kCPL; ++c) qk[gsel][d0 + c] = 0.0f;
+      for (int c = 0; c < kCPL; ++c) {
+        const int d = d0 + c;
+        const uint32_t sw = cur.ks[c / 2], zw = cur.kz[c / 2];
+        const float s = f16_to_f32((c & 1) ? (sw >> 16) : (sw & 0xffffu));
+        const float z = f16_to_f32((c & 1) ? (zw >> 16) : (zw & 0xffffu));
+        const float qv = qs[d];
+        bpart = fmaf(qv, z, bpart);
+        const int pos = (d & ~15) + channel_pos(d & 15);
+        const float f = kKeyComb ? inv_unit : inv_unit * plain_factor(pos & 15);
+        qk[gsel][pos] = gvalid ? qv * s * f : 0.0f;
       }
-      bpart = half_wave_sum(bpart);
+      bpart = half_wave_sum(gvalid ? bpart : 0.0f);
       if ((lane & 31) == 0) bias_s[gsel] = bpart;
     }
     __syncthreads();
@@ -131,38 +252,37 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     // --- scores: one token per lane, keys at the source's full precision
     const int t = t0 + lane;
     const bool valid = t < end;
-    float s_t = -INFINITY;
-    if (valid) {
+    float s_t;
+    {
       const int g = lane >> 5;
-      const uint8_t* blk = hbase + static_cast<int64_t>(bt[t / L.P]) * L.HB;
-      const int r = t % L.P;
-      uint32_t hw[kWords], lw[kWords];
-      const uint4* ph = reinterpret_cast<const uint4*>(blk + L.off_khi + r * L.row);
-#pragma unroll
-      for (int v = 0; v < kWords / 4; ++v) {
-        const uint4 x = ph[v];
-        hw[4 * v] = x.x; hw[4 * v + 1] = x.y; hw[4 * v + 2] = x.z; hw[4 * v + 3] = x.w;
-      }
-      if (kQ4) {
-        const uint4* pl = reinterpret_cast<const uint4*>(blk + L.off_klo + r * L.row);
-#pragma unroll
-        for (int v = 0; v < kWords / 4; ++v) {
-          const uint4 x = pl[v];
-          lw[4 * v] = x.x; lw[4 * v + 1] = x.y; lw[4 * v + 2] = x.z; lw[4 * v + 3] = x.w;
-        }
-      }
+      const float4* qv4 = reinterpret_cast<const float4*>(qk[g]);
       float dot = 0.0f;
 #pragma unroll
       for (int k = 0; k < kWords; ++k) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t cls = kQ4 ? combine(hw[k], lw[k], i) : field(hw[k], i);
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb)
-            dot = fmaf(qk[g][16 * k + 4 * bb + i], byte_f(cls, bb), dot);
+        const uint32_t hw = (&cur.kh[k / 4].x)[k % 4];
+        float f[16];
+        if (kKeyComb) {
+          const uint32_t lw = (&cur.kl[k / 4].x)[k % 4];
+          unpack_combined(hw, lw, f);
+        } else {
+          unpack_plain(hw, f);
         }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4 q4 = qv4[4 * k + v];
+          dot = fmaf(q4.x, f[4 * v], dot);
+          dot = fmaf(q4.y, f[4 * v + 1], dot);
+          dot = fmaf(q4.z, f[4 * v + 2], dot);
+          dot = fmaf(q4.w, f[4 * v + 3], dot);
+        }
+        // keep each word's multiplier reads next to their use (register pressure)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
       }
-      s_t = dot + bias_s[g];
+      // computed for every lane (no branch): keeps the unrolled reads and
+      // arithmetic interleaved instead of sunk into a conditional block
+      asm volatile("" : "+v"(dot));
+      s_t = valid ? dot + bias_s[g] : -INFINITY;
     }
 
     // --- online softmax with a wave-uniform running maximum
@@ -177,52 +297,62 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
     const float p = valid ? __expf(s_t - m) : 0.0f;
     lsum += p;
-    if (kSparse && valid) sc[t - start] = s_t;
+    if (kSparse) {
+      // candidates: tokens that pass tau against the LSE of the tokens seen
+      // so far (this tile included).  That LSE never exceeds the global one,
+      // so no true flag is dropped; the merge kernel takes the exact
+      // decision.  The margin covers rounding of this running test.
+      const float ltot = wave_sum(lsum);
+      const float theta = m + logf(ltot) + a.log_tau - 1e-3f;
+      const bool f = valid && s_t >= theta;
+      const uint64_t bal = __ballot(f);
+      if (f) cand_list[n_cand + __popcll(bal & ((1ull << lane) - 1ull))] = make_int2(t, __float_as_int(s_t));
+      n_cand += __popcll(bal);
+    }
     ptile[lane] = p;
     __syncthreads();
 
     // --- values: lane = (token slot, 32-channel group); high plane only
-    //     (both planes in dense mode)
+    //     (both planes when tau = 0)
 #pragma unroll
-    for (int sub = 0; sub < kTile; sub += kSlots) {
-      const int tt = t0 + sub + vslot;
-      if (tt < end) {
-        const float pp = ptile[sub + vslot];
-        const uint8_t* blk = hbase + static_cast<int64_t>(bt[tt / L.P]) * L.HB;
-        const int r = tt % L.P;
-        const uint32_t meta = reinterpret_cast<const uint32_t*>(blk + L.off_vmeta)[r * kNJ + vj];
-        const float vs = f16_to_f32(meta & 0xffffu), vz = f16_to_f32(meta >> 16);
-        const uint2 hv = *reinterpret_cast<const uint2*>(blk + L.off_vhi + r * L.row + 8 * vj);
-        const uint32_t hw2[2] = {hv.x, hv.y};
-        uint32_t lw2[2] = {0u, 0u};
-        float w;
-        if (kQ4 && kDense) {
-          const uint2 lv = *reinterpret_cast<const uint2*>(blk + L.off_vlo + r * L.row + 8 * vj);
-          lw2[0] = lv.x;
-          lw2[1] = lv.y;
-          w = pp * vs;
-          zs = fmaf(pp, vz, zs);
-        } else if (kQ4) {
-          w = pp * vs * 4.0f;                       // high plane weight 4*s
-          zs = fmaf(pp, fmaf(1.5f, vs, vz), zs);    // bucket centre + zero
+    for (int sub = 0; sub < kSubs; ++sub) {
+      const float pp = ptile[sub * kSlots + vslot];   // 0 for tokens past the end
+      const uint32_t meta = cur.vm[sub];
+      const float vs = f16_to_f32(meta & 0xffffu), vz = f16_to_f32(meta >> 16);
+      float w;
+      if (kValComb) {
+        w = pp * vs;
+        zs = fmaf(pp, vz, zs);
+      } else if (kQ4) {
+        w = pp * vs * 4.0f;                       // high plane weight 4*s
+        zs = fmaf(pp, fmaf(1.5f, vs, vz), zs);    // bucket centre + zero
+      } else {
+        w = pp * vs;
+        zs = fmaf(pp, vz, zs);
+      }
+      w *= inv_unit;
+      const float w4 = w * 0.25f;
+      const uint32_t hv[2] = {cur.vh[sub].x, cur.vh[sub].y};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        float f[16];
+        if (kValComb) {
+          const uint32_t lv = e ? cur.vl[sub].y : cur.vl[sub].x;
+          unpack_combined(hv[e], lv, f);
         } else {
-          w = pp * vs;
-          zs = fmaf(pp, vz, zs);
+          unpack_plain(hv[e], f);
         }
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t cls = (kQ4 && kDense) ? combine(hw2[e], lw2[e], i) : field(hw2[e], i);
-            const float wi = w * ((kQ4 && kDense) ? posf<true>(i) : posf<false>(i));
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-              acc[16 * e + 4 * bb + i] = fmaf(wi, byte_f(cls, bb), acc[16 * e + 4 * bb + i]);
-          }
+        for (int q = 0; q < 16; ++q) {
+          const float wq = kValComb ? w : (((q / 4) & 1) ? w4 : w);
+          acc[16 * e + q] = fmaf(wq, f[q], acc[16 * e + q]);
         }
       }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
+    cur = nxt;
   }
 
   // --- partial: sum the token slots of each channel group
@@ -235,33 +365,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   lsum = wave_sum(lsum);
   if (lane < kNJ) {
 #pragma unroll
-    for (int c = 0; c < 32; ++c) part[kPartialPad + kGroup * lane + c] = acc[c] + zs;
+    for (int c = 0; c < 32; ++c)
+      part[kPartialPad + kGroup * lane + 16 * (c / 16) + pos_channel(c % 16)] = acc[c] + zs;
   }
   if (lane == 0) {
     part[0] = m;
     part[1] = lsum;
   }
 
-  // --- candidates: tokens that pass tau against this split's own LSE.  The
-  //     split's LSE is <= the global one, so no true flag is dropped; the
-  //     merge kernel takes the final decision.  A small margin covers
-  //     rounding of this local test.
-  if (kSparse) {
-    const float theta = m + logf(lsum) + a.log_tau - 1e-3f;
-    int2* cl = a.cand + (pair * a.S + split) * a.split_len;
-    const int n = end - start;
-    int count = 0;
-    for (int base = 0; base < n; base += 64) {
-      const int idx = base + lane;
-      const float v = idx < n ? sc[idx] : -INFINITY;
-      const bool f = v >= theta;
-      const uint64_t bal = __ballot(f);
-      const int pos = __popcll(bal & ((1ull << lane) - 1ull));
-      if (f) cl[count + pos] = make_int2(start + idx, __float_as_int(v));
-      count += __popcll(bal);
-    }
-    if (lane == 0) a.cand_count[pair * a.S + split] = count;
-  }
+  if (kSparse && lane == 0) a.cand_count[pair * a.S + split] = n_cand;
 }
 
 template <int D, int KIND, int MODE>
