@@ -116,9 +116,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
   __shared__ float qs[D];
   __shared__ float qk[2][D];                 // per-channel key multipliers, position order
-  __shared__ float bias_s[2];
   __shared__ float ptile[kTile];
-  __shared__ uint32_t pgoff[kMaxSplitLen / 16];
+  // byte offset of the split's i-th page inside this head's pool region
+  // (+4: the prefetch of the tile after the last one may index past np)
+  __shared__ uint32_t pgoff[kMaxSplitLen / 16 + 4];
 
   const int lane = threadIdx.x;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -139,16 +140,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     return;
   }
 
-  // page size is a power of two; the split starts on a page boundary.
-  // pgoff[i]: byte offset, inside this head's pool region, of the split's
-  // i-th page (physical page * head-block bytes).
+  // page size is a power of two; splits and tiles start on page boundaries
   const int lgP = __builtin_ctz(static_cast<unsigned>(L.P));
   const int pmask = L.P - 1;
   {
     const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_pages + (start >> lgP);
     const int np = ((end - start) + pmask) >> lgP;
-    for (int i = lane; i < np; i += 64)
-      pgoff[i] = static_cast<uint32_t>(bt[i]) * static_cast<uint32_t>(L.HB);
+    for (int i = lane; i < kMaxSplitLen / 16 + 4; i += 64)
+      pgoff[i] = i < np ? static_cast<uint32_t>(bt[i]) * static_cast<uint32_t>(L.HB) : 0u;
   }
   for (int d = lane; d < D; d += 64) qs[d] = bf16_to_f32(a.q[pair * D + d]) * a.sm_scale;
   __syncthreads();
@@ -161,56 +160,73 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int vj = lane % kNJ, vslot = lane / kNJ;
   const int gsel = lane >> 5;
   const int d0 = (lane & 31) * kCPL;
-  const int last = end - 1;
   const float unit = __builtin_amdgcn_cvt_pk_f32_fp8(1, false)[0];
   const float inv_unit = 1.0f / unit;
+  // lane-constant parts of the load offsets
+  const uint32_t lane_krow = static_cast<uint32_t>((lane & pmask) * (D / 4));
+  const int lane_kpage = lane >> lgP;
+  const uint32_t lane_vrow = static_cast<uint32_t>(vslot * (D / 4) + 8 * vj);
+  const uint32_t lane_vmeta = static_cast<uint32_t>((vslot * kNJ + vj) * 4);
+  const int lane_mpage = (kGroup * gsel) >> lgP;
+  const uint32_t lane_kmeta = static_cast<uint32_t>(L.off_kmeta + (((kGroup * gsel) & pmask) / kGroup) * 4 * D + 2 * d0);
 
-  // byte offset of token t's row inside its page's head-block
-  auto row_off = [&](int t) -> uint32_t {
-    return pgoff[(t - start) >> lgP] + static_cast<uint32_t>((t & pmask) * (D / 4));
-  };
-  auto ld128 = [&](uint32_t off) -> uint4 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+  auto ld128 = [&](uint32_t voff, uint32_t soff) -> uint4 {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
   };
-  auto ld64 = [&](uint32_t off) -> uint2 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, 0);
+  auto ld64 = [&](uint32_t voff, uint32_t soff) -> uint2 {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, 0);
     return make_uint2(v[0], v[1]);
   };
-  auto ld32 = [&](uint32_t off) -> uint32_t { return __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0); };
+  auto ld32 = [&](uint32_t voff, uint32_t soff) -> uint32_t {
+    return __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, soff, 0);
+  };
 
-  // Issue every load of the tile starting at t0.  Token indices are clamped
-  // to the split, so every address is valid; clamped lanes are masked later.
+  // Issue every load of the tile starting at t0.  Rows past the split's end
+  // read whatever their (possibly unmapped) page offsets point to inside the
+  // head's region; the buffer bounds keep that safe and the results are
+  // masked out.
   auto fetch = [&](Tile& td, int t0) {
+    const int tp0 = (t0 - start) >> lgP;
     {
-      const uint32_t ro = row_off(min(t0 + lane, last));
+      const uint32_t ro = pgoff[tp0 + lane_kpage] + lane_krow;
 #pragma unroll
-      for (int v = 0; v < D / 64; ++v) td.kh[v] = ld128(ro + L.off_khi + 16 * v);
+      for (int v = 0; v < D / 64; ++v) td.kh[v] = ld128(ro, L.off_khi + 16 * v);
       if (kQ4) {
 #pragma unroll
-        for (int v = 0; v < D / 64; ++v) td.kl[v] = ld128(ro + L.off_klo + 16 * v);
+        for (int v = 0; v < D / 64; ++v) td.kl[v] = ld128(ro, L.off_klo + 16 * v);
       }
     }
 #pragma unroll
     for (int sub = 0; sub < kSubs; ++sub) {
-      const int tt = min(t0 + sub * kSlots + vslot, last);
-      const uint32_t ro = row_off(tt);
-      td.vh[sub] = ld64(ro + L.off_vhi + 8 * vj);
-      if (kDense) td.vl[sub] = ld64(ro + L.off_vlo + 8 * vj);
-      td.vm[sub] = ld32(pgoff[(tt - start) >> lgP] + L.off_vmeta + ((tt & pmask) * kNJ + vj) * 4);
+      const int first = sub * kSlots;
+      if (kSlots <= 16) {
+        // a value step's 16 tokens share one page (pages hold >= 16 tokens):
+        // the page offset is wave-uniform and rides in the scalar offset
+        const uint32_t pg = __builtin_amdgcn_readfirstlane(pgoff[tp0 + (first >> lgP)]);
+        const uint32_t rowbase = pg + static_cast<uint32_t>((first & pmask) * (D / 4));
+        td.vh[sub] = ld64(lane_vrow, rowbase + L.off_vhi);
+        if (kDense) td.vl[sub] = ld64(lane_vrow, rowbase + L.off_vlo);
+        td.vm[sub] = ld32(lane_vmeta, pg + L.off_vmeta + static_cast<uint32_t>((first & pmask) * kNJ * 4));
+      } else {
+        // 32-token steps may span two 16-token pages: per-lane page offset
+        const int tok = first + vslot;
+        const uint32_t pg = pgoff[tp0 + (tok >> lgP)];
+        const uint32_t ro = pg + static_cast<uint32_t>((tok & pmask) * (D / 4) + 8 * vj);
+        td.vh[sub] = ld64(ro, L.off_vhi);
+        if (kDense) td.vl[sub] = ld64(ro, L.off_vlo);
+        td.vm[sub] = ld32(pg + static_cast<uint32_t>(((tok & pmask) * kNJ + vj) * 4), L.off_vmeta);
+      }
     }
     {
-      int gtok = t0 + kGroup * gsel;
-      if (gtok > last) gtok = t0;     // second group absent: read the first (unused)
-      const uint32_t mo = pgoff[(gtok - start) >> lgP] + L.off_kmeta +
-                          ((gtok & pmask) / kGroup) * 4 * D + 2 * d0;
+      const uint32_t mo = pgoff[tp0 + lane_mpage] + lane_kmeta;
       if (D == 128) {
-        const uint2 s2 = ld64(mo), z2 = ld64(mo + 2 * D);
+        const uint2 s2 = ld64(mo, 0), z2 = ld64(mo, 2 * D);
         td.ks[0] = s2.x; td.ks[D / 64 - 1] = s2.y;
         td.kz[0] = z2.x; td.kz[D / 64 - 1] = z2.y;
       } else {
-        td.ks[0] = ld32(mo);
-        td.kz[0] = ld32(mo + 2 * D);
+        td.ks[0] = ld32(mo, 0);
+        td.kz[0] = ld32(mo, 2 * D);
       }
     }
   };
@@ -222,15 +238,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   int2* cand_list = a.cand + (pair * a.S + split) * a.split_len;
   int n_cand = 0;
 
-  Tile cur;
-  fetch(cur, start);
-  for (int t0 = start; t0 < end; t0 += kTile) {
-    Tile nxt;
-    fetch(nxt, t0 + kTile <= last ? t0 + kTile : t0);
-
+  auto compute = [&](const Tile& cur, int t0) {
     // --- key metadata of the tile's two key groups -> per-channel multipliers
+    float bias0, bias1;
     {
-      const bool gvalid = t0 + kGroup * gsel <= last;
+      const bool gvalid = t0 + kGroup * gsel < end;
       float bpart = 0.0f;
 #pragma unroll
       for (int c = 0; c < kCPL; ++c) {
@@ -244,8 +256,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         const float f = kKeyComb ? inv_unit : inv_unit * plain_factor(pos & 15);
         qk[gsel][pos] = gvalid ? qv * s * f : 0.0f;
       }
-      bpart = half_wave_sum(gvalid ? bpart : 0.0f);
-      if ((lane & 31) == 0) bias_s[gsel] = bpart;
+      const float rs = row_sum(gvalid ? bpart : 0.0f);
+      bias0 = lane_f(rs, 0) + lane_f(rs, 16);
+      bias1 = lane_f(rs, 32) + lane_f(rs, 48);
     }
     __syncthreads();
 
@@ -282,11 +295,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       // computed for every lane (no branch): keeps the unrolled reads and
       // arithmetic interleaved instead of sunk into a conditional block
       asm volatile("" : "+v"(dot));
-      s_t = valid ? dot + bias_s[g] : -INFINITY;
+      s_t = valid ? dot + (g ? bias1 : bias0) : -INFINITY;
     }
 
     // --- online softmax with a wave-uniform running maximum
-    const float tmax = wave_max(s_t);
+    const float tmax = dpp_wave_max(s_t);
     if (tmax > m) {
       const float alpha = __expf(m - tmax);
       lsum *= alpha;
@@ -302,7 +315,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       // so far (this tile included).  That LSE never exceeds the global one,
       // so no true flag is dropped; the merge kernel takes the exact
       // decision.  The margin covers rounding of this running test.
-      const float ltot = wave_sum(lsum);
+      const float ltot = dpp_wave_sum(lsum);
       const float theta = m + logf(ltot) + a.log_tau - 1e-3f;
       const bool f = valid && s_t >= theta;
       const uint64_t bal = __ballot(f);
@@ -317,7 +330,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int sub = 0; sub < kSubs; ++sub) {
       const float pp = ptile[sub * kSlots + vslot];   // 0 for tokens past the end
-      const uint32_t meta = cur.vm[sub];
+      // rows past the end hold arbitrary bytes: zero their metadata
+      const uint32_t meta = (t0 + sub * kSlots + vslot < end) ? cur.vm[sub] : 0u;
       const float vs = f16_to_f32(meta & 0xffffu), vz = f16_to_f32(meta >> 16);
       float w;
       if (kValComb) {
@@ -352,7 +366,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-    cur = nxt;
+  };
+
+  // ping-pong over two tile buffers: the next tile's loads are issued before
+  // the current tile computes.  A tile with no successor re-issues its own
+  // loads (cache hits) so that every iteration has the same load pattern.
+  Tile bufA, bufB;
+  fetch(bufA, start);
+  for (int t0 = start;;) {
+    fetch(bufB, t0 + kTile < end ? t0 + kTile : t0);
+    compute(bufA, t0);
+    t0 += kTile;
+    if (t0 >= end) break;
+    fetch(bufA, t0 + kTile < end ? t0 + kTile : t0);
+    compute(bufB, t0);
+    t0 += kTile;
+    if (t0 >= end) break;
   }
 
   // --- partial: sum the token slots of each channel group
@@ -362,7 +391,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     for (int c = 0; c < 32; ++c) acc[c] += __shfl_xor(acc[c], o, 64);
     zs += __shfl_xor(zs, o, 64);
   }
-  lsum = wave_sum(lsum);
+  lsum = dpp_wave_sum(lsum);
   if (lane < kNJ) {
 #pragma unroll
     for (int c = 0; c < 32; ++c)
@@ -372,7 +401,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     part[0] = m;
     part[1] = lsum;
   }
-
   if (kSparse && lane == 0) a.cand_count[pair * a.S + split] = n_cand;
 }
 
