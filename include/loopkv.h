@@ -215,6 +215,16 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells,
  * reused.  Errors: LOOPKV_E_INVAL (bad class or NULL output), LOOPKV_E_HIP.
  */
 enum { LOOPKV_KERNEL_SPLIT = 0, LOOPKV_KERNEL_MERGE = 1, LOOPKV_KERNEL_APPEND = 2 };
+
+/*
+ * Measurement helper (not an operation of the method): reads `bytes` (a
+ * multiple of 16, rounded down) from device buffer `buf` with 16-byte loads
+ * on `stream`, to measure the practical HBM read bandwidth next to the
+ * nominal peak.  `sink` (device, may be NULL) is written only for one
+ * impossible checksum, so the loads cannot be optimized away.
+ * Errors: LOOPKV_E_INVAL (NULL or unaligned buffer), LOOPKV_E_HIP.
+ */
+int loopkv_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 int loopkv_profile_enable(int on);
 int loopkv_profile_collect(int kernel_class, int64_t* launches, double* total_ms);
 

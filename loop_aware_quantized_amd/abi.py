@@ -42,6 +42,7 @@ _SIGNATURES = {
     "loopkv_decode": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "loopkv_profile_enable": (c_int, [c_int]),
     "loopkv_profile_collect": (c_int, [c_int, POINTER(c_int64), POINTER(ctypes.c_double)]),
+    "loopkv_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
 }
 
 KERNEL_SPLIT = 0
@@ -245,3 +246,9 @@ def loopkv_profile_collect(kernel_class: int):
     n, ms = c_int64(), ctypes.c_double()
     _check(lib().loopkv_profile_collect(kernel_class, ctypes.byref(n), ctypes.byref(ms)))
     return n.value, ms.value
+
+
+def loopkv_read_probe(buf, sink=None, stream=None) -> int:
+    """Stream-read a device tensor (bandwidth probe)."""
+    return _check(lib().loopkv_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                          _stream_handle(stream)))

@@ -199,7 +199,29 @@ hipError_t launch_typed(const AppendArgs& a, int batch, hipStream_t stream) {
   return e;
 }
 
+// Streaming-read probe: every lane reads 16-byte words grid-stride; the
+// result is written only for an impossible value so the loads stay live.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n16,
+                                                         uint32_t* sink) {
+  uint32_t acc = 0;
+  size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= a.x ^ b.y ^ c.z ^ d.w;
+  }
+  for (; i < n16; i += stride) acc ^= p[i].x;
+  if (acc == 0x9E3779B9u && sink) sink[0] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const uint4*>(buf), bytes / 16, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t stream) {
   const bool q4 = a.lay.kind == kKindQ4;

@@ -338,14 +338,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         w = pp * vs;
         zs = fmaf(pp, vz, zs);
       } else if (kQ4) {
-        w = pp * vs * 4.0f;                       // high plane weight 4*s
+        w = pp * vs;                              // high plane weight 4*s: x4 in the epilogue
         zs = fmaf(pp, fmaf(1.5f, vs, vz), zs);    // bucket centre + zero
       } else {
         w = pp * vs;
         zs = fmaf(pp, vz, zs);
       }
-      w *= inv_unit;
-      const float w4 = w * 0.25f;
       const uint32_t hv[2] = {cur.vh[sub].x, cur.vh[sub].y};
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -358,8 +356,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const float wq = kValComb ? w : (((q / 4) & 1) ? w4 : w);
-          acc[16 * e + q] = fmaf(wq, f[q], acc[16 * e + q]);
+          acc[16 * e + q] = fmaf(w, f[q], acc[16 * e + q]);
         }
       }
       asm volatile("" ::: "memory");
@@ -395,7 +392,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   if (lane < kNJ) {
 #pragma unroll
     for (int c = 0; c < 32; ++c)
-      part[kPartialPad + kGroup * lane + 16 * (c / 16) + pos_channel(c % 16)] = acc[c] + zs;
+      // constant factors kept out of the token loop: the fp8 unit, the high
+      // plane's weight 4, and the x4 of fields left in bits 2-3 of a byte
+      part[kPartialPad + kGroup * lane + 16 * (c / 16) + pos_channel(c % 16)] =
+          fmaf(acc[c], inv_unit * (kValComb ? 1.0f : plain_factor(c % 16)) * ((kQ4 && !kValComb) ? 4.0f : 1.0f), zs);
   }
   if (lane == 0) {
     part[0] = m;

@@ -59,6 +59,8 @@ enum { kClassSplit = 0, kClassMerge = 1, kClassAppend = 2, kClasses = 3 };
 void prof_mark(int cls, int phase, hipStream_t stream);
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t stream);
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks,
+                             hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int batch, int mode, hipStream_t stream);
 
 }  // namespace lkv

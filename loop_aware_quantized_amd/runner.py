@@ -16,7 +16,9 @@ class CacheState:
     """Pools of every stored cell of a workload, plus batch metadata."""
 
     def __init__(self, w: wl.Workload, device, kinds=None, taus=None, extra_tokens: int = 0,
-                 lengths=None):
+                 lengths=None, only_cells=None):
+        """only_cells: allocate pools for these stored (loop, layer) cells only
+        (decoding a cell whose source has no pool is then an error)."""
         import torch
         self.w = w
         self.device = device
@@ -35,7 +37,8 @@ class CacheState:
         self.block_tables = torch.from_numpy(table).to(device)
         self.max_seq_len = int(self.capacity.max())
         self.stored = [(r, l) for r in range(w.loops) for l in range(w.layers)
-                       if self.kinds[r, l] != wl.KIND_REUSE]
+                       if self.kinds[r, l] != wl.KIND_REUSE
+                       and (only_cells is None or (r, l) in only_cells)]
         self.pools, self.staging = {}, {}
         mems = {}
         for (r, l) in self.stored:
