@@ -213,6 +213,29 @@ class Bench:
         return gbs
 
 
+def recorded_traffic(workload: str):
+    """Per-launch HBM traffic of the split kernel from the committed rocprofv3
+    counter summary, or None when it is absent, for another workload, or
+    taken from kernel sources that have changed since."""
+    import hashlib
+    import os
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"decode_split_traffic_{workload.replace('-', '').replace('.', '')}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            h.update(open(os.path.join(root, src), "rb").read())
+    except (IndexError, KeyError, ValueError, OSError):
+        return None
+    if h.hexdigest()[:16] != rec.get("source_sha256_16"):
+        return None
+    return rec.get("traffic_bytes_per_launch_avg")
+
+
 def cpu_baseline(w, st, kinds, taus, n_samples, dev):
     """Time oracle.attention.decode on (cell, sequence) samples (cache build excluded)."""
     import oracle.attention as oa
@@ -334,7 +357,8 @@ def main():
         "hbm_frac_required": primary["hbm_gbs_required"] / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": sp["achieved_gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": sp["achieved_gbs"] / HBM_PEAK_GBS,
-                     "traffic": None, "launches": sp["launches"],
+                     "traffic": recorded_traffic(w.name), "traffic_unit": "bytes per launch",
+                     "launches": sp["launches"],
                      "avg_launch_us": sp["ms"] * 1e3 / max(sp["launches"], 1),
                      "alg_bytes_per_launch": sp["alg_bytes"] / max(sp["launches"], 1),
                      "measured_read_peak": peak,

@@ -199,27 +199,36 @@ hipError_t launch_typed(const AppendArgs& a, int batch, hipStream_t stream) {
   return e;
 }
 
-// Streaming-read probe: every lane reads 16-byte words grid-stride; the
-// result is written only for an impossible value so the loads stay live.
-__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n16,
-                                                         uint32_t* sink) {
+// Streaming-read probe: each 64-lane workgroup streams one contiguous chunk
+// with four 16-byte loads per lane in flight; the result is written only
+// for an impossible value so the loads stay live.
+constexpr size_t kProbeChunk = 256 << 10;
+
+__global__ __launch_bounds__(64) void read_probe_kernel(const uint8_t* __restrict__ base, size_t bytes,
+                                                        uint32_t* sink) {
+  const size_t begin = blockIdx.x * kProbeChunk;
+  const size_t end = begin + kProbeChunk < bytes ? begin + kProbeChunk : bytes;
+  const int lane = threadIdx.x;
   uint32_t acc = 0;
-  size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
-  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+  size_t off = begin;
+  for (; off + 4096 <= end; off += 4096) {
+    const uint4 a = *reinterpret_cast<const uint4*>(base + off + lane * 16);
+    const uint4 b = *reinterpret_cast<const uint4*>(base + off + 1024 + lane * 16);
+    const uint4 c = *reinterpret_cast<const uint4*>(base + off + 2048 + lane * 16);
+    const uint4 d = *reinterpret_cast<const uint4*>(base + off + 3072 + lane * 16);
     acc ^= a.x ^ b.y ^ c.z ^ d.w;
   }
-  for (; i < n16; i += stride) acc ^= p[i].x;
+  for (off += lane * 16; off + 16 <= end; off += 1024) acc ^= reinterpret_cast<const uint4*>(base + off)->x;
   if (acc == 0x9E3779B9u && sink) sink[0] = acc;
 }
 
 }  // namespace
 
-hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks,
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int /*blocks*/,
                              hipStream_t stream) {
-  hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, stream,
-                     static_cast<const uint4*>(buf), bytes / 16, sink);
+  const size_t chunks = (bytes + kProbeChunk - 1) / kProbeChunk;
+  hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<unsigned>(chunks)), dim3(64), 0, stream,
+                     static_cast<const uint8_t*>(buf), bytes, sink);
   return hipGetLastError();
 }
 
