@@ -112,7 +112,9 @@ class Bench:
             for c in st.stored:
                 k, v = self.new_kv[c]
                 abi.loopkv_append(st.plan, st.cells, c[0], c[1], app, w.append_tokens, k, v)
-        bt = st.batch(self.lens_dev[s + 1] if w.append_tokens else self.lens_dev[0])
+        lens_now = self.lens_of(s) if w.append_tokens else self.lens0
+        bt = st.batch(self.lens_dev[s + 1] if w.append_tokens else self.lens_dev[0],
+                      sum_seq_lens=int(lens_now.sum()))
         o = abi.make_opts(st.workspace, counters=counters, num_splits=self.args.num_splits)
         for (r, l) in self.order:
             abi.loopkv_decode(st.plan, st.cells, r, l, bt, self.queries[(r, l)], self.out, o)

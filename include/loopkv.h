@@ -118,7 +118,9 @@ size_t loopkv_staging_bytes(const loopkv_plan* plan, int loop, int layer,
                             int32_t max_slots);
 
 /* Device workspace bytes loopkv_decode needs for `batch` sequences of at
- * most max_seq_len tokens (any cell of the plan, any split count). */
+ * most max_seq_len tokens (any cell of the plan, any split count).  No
+ * initial contents are needed.  Calls sharing one workspace must not run
+ * concurrently (stream-order them). */
 size_t loopkv_decode_workspace_bytes(const loopkv_plan* plan, int32_t batch,
                                      int32_t max_seq_len);
 
@@ -146,7 +148,10 @@ typedef struct {
                                    physical page (0 <= p < num_pages)        */
   int32_t max_seq_len;          /* host upper bound of the lengths involved
                                    (decode: attended; append: after append)  */
-  int32_t reserved;
+  int32_t sum_seq_lens;         /* optional host hint: sum of the attended
+                                   lengths (0 = unknown).  Decode uses it only
+                                   to size splits for ragged batches; any
+                                   value gives correct results.              */
 } loopkv_batch;
 
 /*

@@ -60,7 +60,7 @@ class Batch(ctypes.Structure):
     """loopkv_batch"""
     _fields_ = [("batch", c_int32), ("max_pages", c_int32), ("seq_lens", c_void_p),
                 ("slots", c_void_p), ("block_tables", c_void_p), ("max_seq_len", c_int32),
-                ("reserved", c_int32)]
+                ("sum_seq_lens", c_int32)]
 
 
 class DecodeOpts(ctypes.Structure):
@@ -197,9 +197,10 @@ def cell_array(plan: Plan, mems: dict):
 
 
 def make_batch(seq_lens, block_tables, max_seq_len: int, slots=None, batch: int | None = None,
-               max_pages: int | None = None) -> Batch:
+               max_pages: int | None = None, sum_seq_lens: int = 0) -> Batch:
     """loopkv_batch over int32 device tensors seq_lens [B], block_tables [B][max_pages]."""
     b = Batch()
+    b.sum_seq_lens = int(sum_seq_lens) if 0 < sum_seq_lens < 2 ** 31 else 0
     b.batch = int(seq_lens.shape[0] if batch is None else batch)
     b.max_pages = int(block_tables.shape[-1] if max_pages is None else max_pages)
     b.seq_lens = _ptr(seq_lens)

@@ -83,20 +83,32 @@ struct Splits {
   int S, len;
 };
 
-Splits choose_splits(int64_t pairs, int t_max, int requested) {
+// Split plan for `batch` sequences x `heads` of at most t_max tokens (sum
+// of lengths t_sum when known, else 0).  One wave runs per non-empty split.
+//  - near-uniform lengths: one round of resident waves (12 per CU), all
+//    splits the same length;
+//  - ragged lengths: about three rounds of non-empty splits, so that waves
+//    that finish early pick up the remaining ones and the tail is short.
+// Automatic splits hold at least 256 tokens (4 tiles); a requested count
+// gives splits of ceil(t_max / count) tokens rounded up to a tile.  No split
+// exceeds kMaxSplitLen.
+Splits choose_splits(int64_t batch, int64_t heads, int t_max, int64_t t_sum, int requested) {
   const int64_t tm = std::max<int64_t>(t_max, 1);
-  int64_t s0;
+  const int64_t pairs = std::max<int64_t>(batch * heads, 1);
+  const int64_t slots = static_cast<int64_t>(cu_count()) * 12;
+  int64_t len;
   if (requested > 0) {
-    s0 = requested;
-  } else {
-    // aim for several resident waves per compute unit
-    const int64_t target = static_cast<int64_t>(cu_count()) * 12;
-    s0 = std::max<int64_t>(1, (target + pairs - 1) / std::max<int64_t>(pairs, 1));
-    // keep splits long enough to amortize the per-split epilogue
-    s0 = std::min<int64_t>(s0, std::max<int64_t>(1, tm / 512));
+    len = round_up((tm + requested - 1) / requested, lkv::kTile);
+    len = std::min<int64_t>(len, lkv::kMaxSplitLen);
+    return {static_cast<int>((tm + len - 1) / len), static_cast<int>(len)};
   }
-  s0 = std::max<int64_t>(s0, (tm + lkv::kMaxSplitLen - 1) / lkv::kMaxSplitLen);
-  int64_t len = round_up((tm + s0 - 1) / s0, lkv::kTile);
+  if (t_sum > 0 && t_sum * 100 < tm * batch * 85) {
+    len = round_up((t_sum * heads + 3 * slots - 1) / (3 * slots), lkv::kTile);
+  } else {
+    const int64_t s0 = (slots + pairs - 1) / pairs;
+    len = round_up((tm + s0 - 1) / s0, lkv::kTile);
+  }
+  len = std::max<int64_t>(len, std::min<int64_t>(256, round_up(tm, lkv::kTile)));
   len = std::min<int64_t>(len, lkv::kMaxSplitLen);
   const int64_t S = (tm + len - 1) / len;
   return {static_cast<int>(S), static_cast<int>(len)};
@@ -415,8 +427,8 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
     const int rc = debug_check(batch, plan->P, mem.num_pages, 0, 0, s);
     if (rc != LOOPKV_OK) return rc;
   }
-  const int64_t pairs = static_cast<int64_t>(batch->batch) * plan->H;
-  const Splits sp = choose_splits(pairs, batch->max_seq_len, opts->num_splits);
+  const Splits sp = choose_splits(batch->batch, plan->H, batch->max_seq_len,
+                                  batch->sum_seq_lens > 0 ? batch->sum_seq_lens : 0, opts->num_splits);
   if (sp.S > lkv::kMaxSplits) return fail(LOOPKV_E_INVAL, "decode: max_seq_len needs too many splits");
 
   int mode = lkv::kModePlain;

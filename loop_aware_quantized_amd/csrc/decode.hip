@@ -12,11 +12,15 @@
 //       are formed, and values are accumulated from the high plane only (or
 //       from both planes when tau = 0).  It writes a partial (max, sum, o)
 //       and, when a tau mask is needed, the compacted list of tokens that
-//       can still pass the threshold (wave ballot + prefix count).
+//       can still pass the threshold (wave ballot + prefix count).  The
+//       first split of a (sequence, head) also clears its mask row.
 //   decode_merge_kernel  one wave per (head, sequence).  Log-sum-exp merge of
 //       the partials; tokens with p_t >= tau (score >= LSE + ln tau) are
 //       flagged with a ballot + prefix count, and only their low-plane rows
 //       are fetched to correct the bucket-centre values.
+// The kernel boundary orders the two: a merge inside the split kernel (last
+// split to arrive) would need a device-scope release per wave, which on
+// this chip writes back the XCD's L2 and measured several times slower.
 // An unfetched 4-bit value is (4*hi + 3/2)*s + z, so a flagged token adds
 // p_t * s * (lo - 3/2).
 //
@@ -100,6 +104,210 @@ struct TileData {
   uint32_t ks[D / 64], kz[D / 64];  // key-group scale / zero of this lane's channels
 };
 
+// One wave per (head, sequence): log-sum-exp merge of the S_used partials,
+// then (sparse mode) the exact test p_t >= tau over the candidate lists,
+// the mask bits and the low-plane correction of the flagged tokens.  The
+// kernel is a chain of dependent reads, so each step issues its reads for
+// many splits / candidates / tokens at once.
+template <int D, int KIND, int MODE>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int kNJ = D / kGroup;
+  constexpr int kSlots = 64 / kNJ;
+  constexpr int kRec = D + kPartialPad;
+  constexpr int kCPL = D / 64;           // output channels per lane
+  constexpr int kPass = 4;               // candidates per lane per scan pass
+  constexpr bool kSparse = MODE == kModeSparse;
+  constexpr bool kDense = MODE == kModeDense;
+  static_assert(kFlagCap >= 2 * 64 * kPass, "flag buffer must hold two scan passes");
+
+  __shared__ float o_s[D];
+  __shared__ int fl_t[kSparse ? kFlagCap : 1];        // flagged tokens awaiting their low rows
+  __shared__ float fl_p[kSparse ? kFlagCap : 1];      // their weights p_t
+  __shared__ uint32_t fl_pg[kSparse ? kFlagCap : 1];  // their page's offset in the head region
+  __shared__ int pre[kSparse ? 64 : 1];               // inclusive prefix of list lengths
+
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const CellLayout L = a.lay;
+  const int T = a.seq_lens[b];
+  const int64_t pair = static_cast<int64_t>(b) * a.H + h;
+  float* outp = a.out + pair * D;
+  if (T <= 0) {
+    for (int d = lane; d < D; d += 64) outp[d] = 0.0f;
+    return;
+  }
+  // lengths above max_seq_len break the caller's contract; never read past S
+  const int S_used = min((T + a.split_len - 1) / a.split_len, a.S);
+  const float* parts = a.partials + pair * a.S * kRec;
+  // the row was cleared by the split kernel (first split of the pair)
+  uint32_t* mrow = a.mask_bits ? a.mask_bits + pair * a.mask_words : nullptr;
+
+  // --- log-sum-exp merge: lanes over splits for (max, sum); lanes over
+  //     channels for o, each split's weight broadcast from its lane
+  float M = -INFINITY;
+  for (int i = lane; i < S_used; i += 64) M = fmaxf(M, parts[i * kRec]);
+  M = wave_max(M);
+  float lsum = 0.0f;
+  for (int i = lane; i < S_used; i += 64) lsum = fmaf(__expf(parts[i * kRec] - M), parts[i * kRec + 1], lsum);
+  lsum = wave_sum(lsum);
+  const float inv = 1.0f / lsum;
+  const float lse = M + logf(lsum);
+  {
+    float o[kCPL];
+#pragma unroll
+    for (int c = 0; c < kCPL; ++c) o[c] = 0.0f;
+    for (int i0 = 0; i0 < S_used; i0 += 64) {
+      const int n = min(64, S_used - i0);
+      const float e_l = lane < n ? __expf(parts[(i0 + lane) * kRec] - M) : 0.0f;
+      // eight records per step, all loads issued before the first use
+      for (int j = 0; j < n; j += 8) {
+        float v[8][kCPL];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float* rec = parts + (i0 + j + u) * kRec + kPartialPad;
+#pragma unroll
+          for (int c = 0; c < kCPL; ++c) v[u][c] = (j + u < n) ? rec[lane + 64 * c] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float e = lane_f(e_l, (j + u) & 63);   // 0 past n
+#pragma unroll
+          for (int c = 0; c < kCPL; ++c) o[c] = fmaf(e, v[u][c], o[c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kCPL; ++c) o_s[lane + 64 * c] = o[c] * inv;
+  }
+
+  unsigned long long flagged = 0ull;
+  if (kSparse) {
+    const float theta = lse + a.log_tau;
+    const int lgP = __builtin_ctz(static_cast<unsigned>(L.P));
+    const int pmask = L.P - 1;
+    const uint8_t* head = a.pool + static_cast<int64_t>(h) * a.num_pages * L.HB;
+    const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_pages;
+    const int vj = lane % kNJ, vslot = lane / kNJ;
+    float corr[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) corr[c] = 0.0f;
+    float cs = 0.0f;
+    int nf = 0;
+
+    // low-plane rows of the buffered flagged tokens: their page offsets
+    // first (all table reads in flight), then lane = (token slot, 32-channel
+    // group) accumulates p_t * s * lo
+    auto gather = [&](int count) {
+      __syncthreads();
+      for (int idx = lane; idx < count; idx += 64)
+        fl_pg[idx] = static_cast<uint32_t>(bt[fl_t[idx] >> lgP]) * static_cast<uint32_t>(L.HB);
+      __syncthreads();
+      for (int base = 0; base < count; base += kSlots) {
+        const int idx = base + vslot;
+        if (idx < count) {
+          const int r = fl_t[idx] & pmask;
+          const float pp = fl_p[idx];
+          const uint8_t* blk = head + fl_pg[idx];
+          const uint32_t meta = reinterpret_cast<const uint32_t*>(blk + L.off_vmeta)[r * kNJ + vj];
+          const float vs = f16_to_f32(meta & 0xffffu);
+          const uint2 lv = *reinterpret_cast<const uint2*>(blk + L.off_vlo + r * L.row + 8 * vj);
+          const uint32_t lw2[2] = {lv.x, lv.y};
+          const float w = pp * vs;
+          cs += w;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t cls = field(lw2[e], i);
+              const float wi = w * posf<false>(i);
+#pragma unroll
+              for (int bb = 0; bb < 4; ++bb)
+                corr[16 * e + 4 * bb + i] = fmaf(wi, byte_f(cls, bb), corr[16 * e + 4 * bb + i]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    };
+
+    // The lists of up to 64 splits are scanned as one flat sequence, kPass
+    // entries per lane per pass: entry k finds its split by binary search
+    // over the inclusive prefix of the list lengths.
+    for (int i0 = 0; i0 < S_used; i0 += 64) {
+      const int ns = min(64, S_used - i0);
+      const int cnt = lane < ns ? a.cand_count[pair * a.S + i0 + lane] : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const int total = __shfl(incl, 63, 64);
+      pre[lane] = incl;
+      __syncthreads();
+      for (int base = 0; base < total; base += 64 * kPass) {
+        if (nf > kFlagCap - 64 * kPass) {
+          gather(nf);
+          flagged += nf;
+          nf = 0;
+        }
+        int2 c[kPass];
+#pragma unroll
+        for (int u = 0; u < kPass; ++u) {
+          const int k = base + 64 * u + lane;
+          c[u] = make_int2(0, 0);
+          if (k < total) {
+            int lo = 0, hi = ns - 1;
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if (pre[mid] > k) hi = mid;
+              else lo = mid + 1;
+            }
+            const int before = lo ? pre[lo - 1] : 0;
+            c[u] = a.cand[(pair * a.S + i0 + lo) * a.split_len + (k - before)];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kPass; ++u) {
+          const int k = base + 64 * u + lane;
+          const float sc = __int_as_float(c[u].y);
+          const bool f = (k < total) && (sc >= theta);
+          const uint64_t bal = __ballot(f);
+          if (f) {
+            const int pos = nf + __popcll(bal & ((1ull << lane) - 1ull));
+            fl_t[pos] = c[u].x;
+            fl_p[pos] = expf(sc - lse);
+            if (mrow && (c[u].x >> 5) < a.mask_words) atomicOr(&mrow[c[u].x >> 5], 1u << (c[u].x & 31));
+          }
+          nf += __popcll(bal);
+        }
+      }
+      __syncthreads();
+    }
+    gather(nf);
+    flagged += nf;
+
+#pragma unroll
+    for (int o = kNJ; o < 64; o <<= 1) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) corr[c] += __shfl_xor(corr[c], o, 64);
+      cs += __shfl_xor(cs, o, 64);
+    }
+    if (lane < kNJ) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) o_s[kGroup * lane + c] += corr[c] - 1.5f * cs;
+    }
+  } else if (kDense) {
+    flagged = static_cast<unsigned long long>(T);
+  }
+  if (a.counters && lane == 0 && (kSparse || kDense)) {
+    atomicAdd(&a.counters[0], flagged);
+    atomicAdd(&a.counters[1], flagged * static_cast<unsigned long long>(L.row));
+  }
+  __syncthreads();
+  for (int d = lane; d < D; d += 64) outp[d] = o_s[d];
+}
+
 template <int D, int KIND, int MODE>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   constexpr int kNJ = D / kGroup;       // value channel groups
@@ -130,15 +338,20 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int end = min(start + a.split_len, T);
   const int64_t pair = static_cast<int64_t>(b) * H + h;
   float* part = a.partials + (pair * a.S + split) * (D + kPartialPad);
-  if (start >= end) {
-    if (lane == 0) {
-      part[0] = -INFINITY;
-      part[1] = 0.0f;
-      if (kSparse) a.cand_count[pair * a.S + split] = 0;
+  if (split == 0 && a.mask_bits) {
+    // the first split owns the pair's mask row: cleared here (all ones up to
+    // T for tau = 0); the merge kernel, launched after, sets the flag bits
+    uint32_t* mrow = a.mask_bits + pair * a.mask_words;
+    for (int w = lane; w < a.mask_words; w += 64) {
+      uint32_t bits = 0u;
+      if (kDense) {
+        const int lo = 32 * w;
+        bits = T >= lo + 32 ? 0xffffffffu : (T > lo ? ((1u << (T - lo)) - 1u) : 0u);
+      }
+      mrow[w] = bits;
     }
-    for (int d = lane; d < D; d += 64) part[kPartialPad + d] = 0.0f;
-    return;
   }
+  if (start >= end) return;   // splits past the end take no part in the merge
 
   // page size is a power of two; splits and tiles start on page boundaries
   const int lgP = __builtin_ctz(static_cast<unsigned>(L.P));
@@ -402,159 +615,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     part[1] = lsum;
   }
   if (kSparse && lane == 0) a.cand_count[pair * a.S + split] = n_cand;
-}
-
-template <int D, int KIND, int MODE>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int kNJ = D / kGroup;
-  constexpr int kSlots = 64 / kNJ;
-  constexpr bool kSparse = MODE == kModeSparse;
-  constexpr bool kDense = MODE == kModeDense;
-
-  __shared__ float ew[kMaxSplits];
-  __shared__ float o_s[D];
-  __shared__ int fl_t[kSparse ? kFlagCap : 1];
-  __shared__ float fl_p[kSparse ? kFlagCap : 1];
-
-  const int lane = threadIdx.x;
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int H = a.H;
-  const CellLayout L = a.lay;
-  const int T = a.seq_lens[b];
-  const int64_t pair = static_cast<int64_t>(b) * H + h;
-  float* outp = a.out + pair * D;
-  uint32_t* mrow = a.mask_bits ? a.mask_bits + pair * a.mask_words : nullptr;
-
-  if (mrow) {
-    for (int w = lane; w < a.mask_words; w += 64) {
-      uint32_t bits = 0u;
-      if (kDense) {
-        const int lo = 32 * w;
-        bits = T >= lo + 32 ? 0xffffffffu : (T > lo ? ((1u << (T - lo)) - 1u) : 0u);
-      }
-      mrow[w] = bits;
-    }
-    __threadfence();
-  }
-  if (T <= 0) {
-    for (int d = lane; d < D; d += 64) outp[d] = 0.0f;
-    return;
-  }
-
-  // lengths above max_seq_len break the caller's contract; never read past S
-  const int S_used = min((T + a.split_len - 1) / a.split_len, a.S);
-  const float* parts = a.partials + pair * a.S * (D + kPartialPad);
-  constexpr int kRec = D + kPartialPad;
-
-  float M = -INFINITY;
-  for (int i = lane; i < S_used; i += 64) M = fmaxf(M, parts[i * kRec]);
-  M = wave_max(M);
-  float lsum = 0.0f;
-  for (int i = lane; i < S_used; i += 64) {
-    const float e = __expf(parts[i * kRec] - M);
-    ew[i] = e;
-    lsum = fmaf(e, parts[i * kRec + 1], lsum);
-  }
-  lsum = wave_sum(lsum);
-  __syncthreads();
-  const float inv = 1.0f / lsum;
-  const float lse = M + logf(lsum);
-  for (int d = lane; d < D; d += 64) {
-    float o = 0.0f;
-    for (int i = 0; i < S_used; ++i) o = fmaf(ew[i], parts[i * kRec + kPartialPad + d], o);
-    o_s[d] = o * inv;
-  }
-
-  unsigned long long flagged = 0ull;
-  if (kSparse) {
-    const float theta = lse + a.log_tau;
-    const int vj = lane % kNJ, vslot = lane / kNJ;
-    float corr[32];
-#pragma unroll
-    for (int c = 0; c < 32; ++c) corr[c] = 0.0f;
-    float cs = 0.0f;
-    int nf = 0;
-
-    auto gather = [&](int count) {
-      for (int base = 0; base < count; base += kSlots) {
-        const int idx = base + vslot;
-        if (idx < count) {
-          const int t = fl_t[idx];
-          const float pp = fl_p[idx];
-          const uint8_t* blk = a.pool + (static_cast<int64_t>(h) * a.num_pages +
-                                         a.block_tables[static_cast<int64_t>(b) * a.max_pages + t / L.P]) * L.HB;
-          const int r = t % L.P;
-          const uint32_t meta = reinterpret_cast<const uint32_t*>(blk + L.off_vmeta)[r * kNJ + vj];
-          const float vs = f16_to_f32(meta & 0xffffu);
-          const uint2 lv = *reinterpret_cast<const uint2*>(blk + L.off_vlo + r * L.row + 8 * vj);
-          const uint32_t lw2[2] = {lv.x, lv.y};
-          const float w = pp * vs;
-          cs += w;
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t cls = field(lw2[e], i);
-              const float wi = w * posf<false>(i);
-#pragma unroll
-              for (int bb = 0; bb < 4; ++bb)
-                corr[16 * e + 4 * bb + i] = fmaf(wi, byte_f(cls, bb), corr[16 * e + 4 * bb + i]);
-            }
-          }
-        }
-      }
-    };
-
-    for (int i = 0; i < S_used; ++i) {
-      const int cnt = a.cand_count[pair * a.S + i];
-      const int2* cl = a.cand + (pair * a.S + i) * a.split_len;
-      for (int base = 0; base < cnt; base += 64) {
-        const int k = base + lane;
-        int2 c = make_int2(0, 0);
-        if (k < cnt) c = cl[k];
-        const float s = __int_as_float(c.y);
-        const bool f = (k < cnt) && (s >= theta);
-        const uint64_t bal = __ballot(f);
-        const int pos = __popcll(bal & ((1ull << lane) - 1ull));
-        if (f) {
-          fl_t[nf + pos] = c.x;
-          fl_p[nf + pos] = expf(s - lse);
-          if (mrow && (c.x >> 5) < a.mask_words) atomicOr(&mrow[c.x >> 5], 1u << (c.x & 31));
-        }
-        nf += __popcll(bal);
-        if (nf > kFlagCap - 64) {
-          __syncthreads();
-          gather(nf);
-          flagged += nf;
-          nf = 0;
-          __syncthreads();
-        }
-      }
-    }
-    __syncthreads();
-    gather(nf);
-    flagged += nf;
-
-#pragma unroll
-    for (int o = kNJ; o < 64; o <<= 1) {
-#pragma unroll
-      for (int c = 0; c < 32; ++c) corr[c] += __shfl_xor(corr[c], o, 64);
-      cs += __shfl_xor(cs, o, 64);
-    }
-    __syncthreads();
-    if (lane < kNJ) {
-#pragma unroll
-      for (int c = 0; c < 32; ++c) o_s[kGroup * lane + c] += corr[c] - 1.5f * cs;
-    }
-  } else if (kDense) {
-    flagged = static_cast<unsigned long long>(T);
-  }
-  if (a.counters && lane == 0 && (kSparse || kDense)) {
-    atomicAdd(&a.counters[0], flagged);
-    atomicAdd(&a.counters[1], flagged * static_cast<unsigned long long>(L.row));
-  }
-  __syncthreads();
-  for (int d = lane; d < D; d += 64) outp[d] = o_s[d];
 }
 
 template <int D, int KIND, int MODE>

@@ -100,9 +100,10 @@ class CacheState:
         return kept
 
     # ---------------------------------------------------------------- decode
-    def batch(self, lens=None, max_seq_len=None):
+    def batch(self, lens=None, max_seq_len=None, sum_seq_lens: int = 0):
         return abi.make_batch(self.lens if lens is None else lens, self.block_tables,
-                              self.max_seq_len if max_seq_len is None else max_seq_len)
+                              self.max_seq_len if max_seq_len is None else max_seq_len,
+                              sum_seq_lens=sum_seq_lens)
 
     def new_mask(self):
         import torch
@@ -110,10 +111,15 @@ class CacheState:
         return torch.zeros(self.w.batch, self.w.heads, words, dtype=torch.int32, device=self.device)
 
     def decode(self, r: int, l: int, q, out, num_splits: int = 0, mask=None, counters=None,
-               lens=None, sm_scale: float = 1.0):
+               lens=None, sm_scale: float = 1.0, sum_seq_lens: int | None = None):
+        """Decode cell (r, l).  sum_seq_lens is the host-side length hint; by
+        default the prefill lengths' sum when lens is None, else 0 (unknown)."""
         opts = abi.make_opts(self.workspace, sm_scale=sm_scale, num_splits=num_splits,
                              mask_bits=mask, counters=counters)
-        return abi.loopkv_decode(self.plan, self.cells, r, l, self.batch(lens), q, out, opts)
+        if sum_seq_lens is None:
+            sum_seq_lens = int(self.lens0.sum()) if lens is None else 0
+        return abi.loopkv_decode(self.plan, self.cells, r, l, self.batch(lens, sum_seq_lens=sum_seq_lens),
+                                 q, out, opts)
 
     def append(self, r: int, l: int, k, v, lens_before):
         batch = abi.make_batch(lens_before, self.block_tables, self.max_seq_len)

@@ -86,7 +86,7 @@ def _run(w, seqs, taus=None, append=False, tau_sweep=()):
             q = wl.cell_query(w, st.cell_index(r, l), DEV)[1]
             out = torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=DEV)
             mask = st.new_mask()
-            st.decode(r, l, q, out, mask=mask, lens=lens_dev)
+            st.decode(r, l, q, out, mask=mask, lens=lens_dev, sum_seq_lens=int(lens.sum()))
             torch.cuda.synchronize()
             src = oa.resolve_source(st.kinds, r, l)
             s = compare_decode(st, r, l, q, out, mask, kept[src], seqs, lens=lens)
