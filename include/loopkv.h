@@ -160,7 +160,7 @@ typedef struct {
  * Source: LoopKV abstract (cells stored at 4 or 2 bits; 4-bit values kept
  * as separately readable high and low bit planes).
  * k_bf16, v_bf16: device [B][n_new][H][D] bfloat16 (raw keys and values of
- *   tokens seq_lens[b] .. seq_lens[b]+n_new-1).
+ *   tokens seq_lens[b] .. seq_lens[b]+n_new-1), 16-byte aligned.
  * Effects: value rows and metadata of the new tokens; key codes and key
  *   metadata of every key group the new tokens touch (the open group of a
  *   sequence is re-quantized over all its tokens, read back from staging);
@@ -169,6 +169,7 @@ typedef struct {
  *   be finite with |x| <= 32768.
  * Returns LOOPKV_NOOP_REUSE (nothing launched) for a reuse cell.
  * Errors: LOOPKV_E_INVAL (bad cell, NULL pool/staging, n_new < 1,
+ *   misaligned inputs,
  *   batch > max_slots when slots == NULL, max_pages * P < max_seq_len),
  *   LOOPKV_E_HIP.
  */

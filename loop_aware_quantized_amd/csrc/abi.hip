@@ -360,6 +360,8 @@ int loopkv_append(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
   if (n_new < 1) return fail(LOOPKV_E_INVAL, "append: n_new must be >= 1");
   if (batch->batch == 0) return LOOPKV_OK;
   if (!k_bf16 || !v_bf16) return fail(LOOPKV_E_INVAL, "append: NULL key or value input");
+  if ((reinterpret_cast<uintptr_t>(k_bf16) | reinterpret_cast<uintptr_t>(v_bf16)) % 16 != 0)
+    return fail(LOOPKV_E_INVAL, "append: key and value inputs must be 16-byte aligned");
   if (!batch->seq_lens || !batch->block_tables)
     return fail(LOOPKV_E_INVAL, "append: NULL seq_lens or block_tables");
   if (batch->max_pages < 1) return fail(LOOPKV_E_INVAL, "append: max_pages must be >= 1");

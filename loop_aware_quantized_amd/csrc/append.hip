@@ -23,6 +23,8 @@ __global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
   constexpr float kLevels = (KIND == kKindQ4) ? 15.0f : 3.0f;
   constexpr int kWords = D / 16;   // 16 two-bit fields per 32-bit word
   constexpr int kNJ = D / kGroup;  // value channel groups
+  constexpr int kRowChunks = D / 8;                   // 16-byte chunks per bf16 key row
+  constexpr int kChunks = kGroup * kRowChunks / 64;   // chunks per lane for a full group
   __shared__ float raw[kGroup][D];
   __shared__ float ks[D], kz[D];
 
@@ -42,29 +44,53 @@ __global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_pages;
   uint8_t* hbase = a.pool + static_cast<int64_t>(h) * a.num_pages * L.HB;
   uint16_t* stg = a.staging + (static_cast<int64_t>(slot) * H + h) * kGroup * D;
+  // the group's tokens lie in page gs/P, and in the next one when P = 16
+  // (read only if the group reaches into it)
+  const int lp = gs / L.P;
+  const int64_t pg_first = bt[lp];
+  const int64_t pg_second = (L.P < kGroup && gs + L.P < ge) ? bt[lp + 1] : pg_first;
+  auto page_of = [&](int t) -> uint8_t* {
+    return hbase + ((t - gs) < L.P ? pg_first : pg_second) * L.HB;
+  };
+  auto new_row = [&](int t) -> int64_t {   // element offset of new token t's (b, h) row
+    return ((static_cast<int64_t>(b) * a.n_new + (t - T0)) * H + h) * D;
+  };
 
-  // raw keys of the group: staged (old) tokens, then new tokens
-  for (int idx = lane; idx < n * (D / 2); idx += 64) {
-    const int i = idx / (D / 2), pr = idx % (D / 2);
-    const int t = gs + i;
-    uint32_t w;
-    if (t < T0) {
-      w = reinterpret_cast<const uint32_t*>(stg)[i * (D / 2) + pr];
-    } else {
-      const int64_t src = ((static_cast<int64_t>(b) * a.n_new + (t - T0)) * H + h) * (D / 2) + pr;
-      w = reinterpret_cast<const uint32_t*>(a.k_in)[src];
+  // raw keys of the group in 16-byte chunks, staged (old) tokens then new
+  // tokens; every load is issued before the first is used
+  {
+    uint4 ch[kChunks];
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u) {
+      const int c = lane + 64 * u;
+      const int i = c / kRowChunks, q = c % kRowChunks;
+      const int t = gs + i;
+      ch[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < n) {
+        const uint16_t* row = t < T0 ? stg + i * D : a.k_in + new_row(t);
+        ch[u] = reinterpret_cast<const uint4*>(row)[q];
+      }
     }
-    raw[i][2 * pr] = bf16_to_f32(static_cast<uint16_t>(w & 0xffffu));
-    raw[i][2 * pr + 1] = bf16_to_f32(static_cast<uint16_t>(w >> 16));
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u) {
+      const int c = lane + 64 * u;
+      const int i = c / kRowChunks, q = c % kRowChunks;
+      if (i < n) {
+        const uint32_t w[4] = {ch[u].x, ch[u].y, ch[u].z, ch[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          raw[i][8 * q + 2 * e] = bf16_to_f32(static_cast<uint16_t>(w[e] & 0xffffu));
+          raw[i][8 * q + 2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(w[e] >> 16));
+        }
+      }
+    }
   }
   __syncthreads();
 
   // key metadata: one channel per lane
   {
-    const int lp = gs / L.P;
     const int kslot = (gs % L.P) / kGroup;
-    uint16_t* km = reinterpret_cast<uint16_t*>(
-        hbase + static_cast<int64_t>(bt[lp]) * L.HB + L.off_kmeta + kslot * 4 * D);
+    uint16_t* km = reinterpret_cast<uint16_t*>(page_of(gs) + L.off_kmeta + kslot * 4 * D);
     for (int d = lane; d < D; d += 64) {
       float mn = raw[0][d], mx = mn;
       for (int i = 1; i < n; ++i) {
@@ -100,7 +126,7 @@ __global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
       }
     }
     const int r = t % L.P;
-    uint8_t* blk = hbase + static_cast<int64_t>(bt[t / L.P]) * L.HB;
+    uint8_t* blk = page_of(t);
     reinterpret_cast<uint32_t*>(blk + L.off_khi + r * L.row)[k] = whi;
     if (KIND == kKindQ4) reinterpret_cast<uint32_t*>(blk + L.off_klo + r * L.row)[k] = wlo;
   }
@@ -111,14 +137,17 @@ __global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
   for (int idx = lane; idx < nv * kNJ; idx += 64) {
     const int i = idx / kNJ, j = idx % kNJ;
     const int t = first_new + i;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.v_in) +
-        (((static_cast<int64_t>(b) * a.n_new + (t - T0)) * H + h) * D + kGroup * j) / 2;
+    const uint4* src = reinterpret_cast<const uint4*>(a.v_in + new_row(t) + kGroup * j);
     float x[kGroup];
 #pragma unroll
-    for (int e = 0; e < kGroup / 2; ++e) {
-      const uint32_t w = src[e];
-      x[2 * e] = bf16_to_f32(static_cast<uint16_t>(w & 0xffffu));
-      x[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(w >> 16));
+    for (int e = 0; e < kGroup / 8; ++e) {
+      const uint4 v4 = src[e];
+      const uint32_t w[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        x[8 * e + 2 * f] = bf16_to_f32(static_cast<uint16_t>(w[f] & 0xffffu));
+        x[8 * e + 2 * f + 1] = bf16_to_f32(static_cast<uint16_t>(w[f] >> 16));
+      }
     }
     float mn = x[0], mx = x[0];
 #pragma unroll
@@ -139,7 +168,7 @@ __global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
       }
     }
     const int r = t % L.P;
-    uint8_t* blk = hbase + static_cast<int64_t>(bt[t / L.P]) * L.HB;
+    uint8_t* blk = page_of(t);
     *reinterpret_cast<uint2*>(blk + L.off_vhi + r * L.row + 8 * j) = make_uint2(hi[0], hi[1]);
     if (KIND == kKindQ4)
       *reinterpret_cast<uint2*>(blk + L.off_vlo + r * L.row + 8 * j) = make_uint2(lo[0], lo[1]);
@@ -152,12 +181,10 @@ __global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
   // one-token append); otherwise append_staging_kernel runs afterwards, so
   // no wave overwrites staging rows another wave still reads.
   if (g == g0 && ge == T1 && (T1 % kGroup) != 0) {
-    for (int idx = lane; idx < (ge - first_new) * (D / 2); idx += 64) {
-      const int i = idx / (D / 2), pr = idx % (D / 2);
+    for (int idx = lane; idx < (ge - first_new) * kRowChunks; idx += 64) {
+      const int i = idx / kRowChunks, q = idx % kRowChunks;
       const int t = first_new + i;
-      const int64_t src = ((static_cast<int64_t>(b) * a.n_new + (t - T0)) * H + h) * (D / 2) + pr;
-      reinterpret_cast<uint32_t*>(stg)[(t - gs) * (D / 2) + pr] =
-          reinterpret_cast<const uint32_t*>(a.k_in)[src];
+      reinterpret_cast<uint4*>(stg + (t - gs) * D)[q] = reinterpret_cast<const uint4*>(a.k_in + new_row(t))[q];
     }
   }
 }

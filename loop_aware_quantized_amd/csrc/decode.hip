@@ -35,6 +35,7 @@ namespace lkv {
 namespace {
 
 constexpr int kFlagCap = 512;      // flagged tokens buffered per gather pass
+constexpr int kCandCap = 256;      // candidates buffered in LDS per split wave
 
 // multiplier of a field at position i of its byte.  "combined" bytes hold a
 // 4-bit code (4*hi + lo) built from two planes: positions 0..2 hold
@@ -328,6 +329,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // byte offset of the split's i-th page inside this head's pool region
   // (+4: the prefetch of the tile after the last one may index past np)
   __shared__ uint32_t pgoff[kMaxSplitLen / 16 + 4];
+  __shared__ int2 cbuf[kSparse ? kCandCap : 1];   // candidate (token, score bits)
 
   const int lane = threadIdx.x;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -448,8 +450,34 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   float acc[32];
 #pragma unroll
   for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
+  // Candidates collect in LDS (cbuf, n_buf entries).  When a tile's new ones
+  // do not fit, the buffer is first re-tested against the running threshold,
+  // which only rises; if still full it spills to the global list (n_glob).
   int2* cand_list = a.cand + (pair * a.S + split) * a.split_len;
-  int n_cand = 0;
+  int n_buf = 0, n_glob = 0;
+  auto compact = [&](float th) {
+    int n = 0;
+    for (int base = 0; base < n_buf; base += 64) {
+      const int idx = base + lane;
+      int2 e = make_int2(0, 0);
+      bool keep = false;
+      if (idx < n_buf) {
+        e = cbuf[idx];
+        keep = __int_as_float(e.y) >= th;
+      }
+      const uint64_t kb = __ballot(keep);
+      // in place: a kept entry moves to n + rank <= idx, never onto an entry
+      // not yet read
+      if (keep) cbuf[n + __popcll(kb & ((1ull << lane) - 1ull))] = e;
+      n += __popcll(kb);
+    }
+    n_buf = n;
+  };
+  auto spill = [&]() {
+    for (int idx = lane; idx < n_buf; idx += 64) cand_list[n_glob + idx] = cbuf[idx];
+    n_glob += n_buf;
+    n_buf = 0;
+  };
 
   auto compute = [&](const Tile& cur, int t0) {
     // --- key metadata of the tile's two key groups -> per-channel multipliers
@@ -532,8 +560,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       const float theta = m + logf(ltot) + a.log_tau - 1e-3f;
       const bool f = valid && s_t >= theta;
       const uint64_t bal = __ballot(f);
-      if (f) cand_list[n_cand + __popcll(bal & ((1ull << lane) - 1ull))] = make_int2(t, __float_as_int(s_t));
-      n_cand += __popcll(bal);
+      const int nb = __popcll(bal);
+      if (n_buf + nb > kCandCap) {
+        compact(theta);
+        if (n_buf + nb > kCandCap) spill();
+      }
+      if (f) cbuf[n_buf + __popcll(bal & ((1ull << lane) - 1ull))] = make_int2(t, __float_as_int(s_t));
+      n_buf += nb;
     }
     ptile[lane] = p;
     __syncthreads();
@@ -614,7 +647,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     part[0] = m;
     part[1] = lsum;
   }
-  if (kSparse && lane == 0) a.cand_count[pair * a.S + split] = n_cand;
+  if (kSparse) {
+    // final test against this split's own LSE (still <= the global one)
+    compact(m + logf(lsum) + a.log_tau - 1e-3f);
+    spill();
+    if (lane == 0) a.cand_count[pair * a.S + split] = n_glob;
+  }
 }
 
 template <int D, int KIND, int MODE>

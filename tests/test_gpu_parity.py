@@ -121,6 +121,23 @@ def test_split_counts_and_page_shuffle():
             assert np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("tau", [1e-4, 1e-3])
+def test_small_tau_candidate_spill(tau):
+    """Thresholds so low that a split's candidates overflow the on-chip
+    buffer (one 4096-token split: up to 1/tau survivors) still flag exactly
+    the oracle's tokens."""
+    w = wl.Workload("spill", 170, batch=2, loops=1, layers=2, heads=2, head_dim=128, page=32,
+                    ctx=4096, heavy_frac=0.0)
+    st = runner.CacheState(w, DEV, [[Q4, Q4]], [[tau, tau]], lengths=[4096, 3001])
+    kept = st.prefill({c: set(range(2)) for c in st.stored})
+    for l in range(2):
+        for ns in (1, 0):
+            q, out, mask, cnt = _decode(st, 0, l, num_splits=ns)
+            s = compare_decode(st, 0, l, q, out, mask, kept[(0, l)], range(2))
+            say(f"  tau {tau} splits {ns}: rel err {s['rel']:.2e} flagged {s['flagged']} band {s['band']}")
+            assert s["flagged"] > 0
+
+
 def test_decode_is_deterministic():
     w = wl.Workload("determ", 150, batch=2, loops=1, layers=1, heads=4, head_dim=128, page=32,
                     ctx=5000, heavy_frac=0.01)
