@@ -90,6 +90,12 @@ __device__ __forceinline__ void unpack_combined(uint32_t h, uint32_t l, float* f
 __host__ __device__ constexpr int pos_channel(int p) { return 4 * (p % 4) + p / 4; }
 __host__ __device__ constexpr int channel_pos(int m) { return 4 * (m % 4) + m / 4; }
 __device__ __forceinline__ constexpr float plain_factor(int p) { return ((p / 4) & 1) ? 0.25f : 1.0f; }
+// value position p = 4i + b accumulated as fp16 subnormals code * 4^i * 2^-24
+__device__ __forceinline__ constexpr float dot2_factor(int p) {
+  return 16777216.0f / static_cast<float>(1 << (2 * (p / 4)));
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 // Everything one 64-token tile reads from HBM, held in registers so the next
 // tile's loads are in flight while the current tile computes.
@@ -573,40 +579,67 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
     // --- values: lane = (token slot, 32-channel group); high plane only
     //     (both planes when tau = 0)
+    if constexpr (kValComb) {
 #pragma unroll
-    for (int sub = 0; sub < kSubs; ++sub) {
-      const float pp = ptile[sub * kSlots + vslot];   // 0 for tokens past the end
-      // rows past the end hold arbitrary bytes: zero their metadata
-      const uint32_t meta = (t0 + sub * kSlots + vslot < end) ? cur.vm[sub] : 0u;
-      const float vs = f16_to_f32(meta & 0xffffu), vz = f16_to_f32(meta >> 16);
-      float w;
-      if (kValComb) {
-        w = pp * vs;
+      for (int sub = 0; sub < kSubs; ++sub) {
+        const float pp = ptile[sub * kSlots + vslot];   // 0 for tokens past the end
+        // rows past the end hold arbitrary bytes: zero their metadata
+        const uint32_t meta = (t0 + sub * kSlots + vslot < end) ? cur.vm[sub] : 0u;
+        const float vs = f16_to_f32(meta & 0xffffu), vz = f16_to_f32(meta >> 16);
+        const float w = pp * vs;
         zs = fmaf(pp, vz, zs);
-      } else if (kQ4) {
-        w = pp * vs;                              // high plane weight 4*s: x4 in the epilogue
-        zs = fmaf(pp, fmaf(1.5f, vs, vz), zs);    // bucket centre + zero
-      } else {
-        w = pp * vs;
-        zs = fmaf(pp, vz, zs);
-      }
-      const uint32_t hv[2] = {cur.vh[sub].x, cur.vh[sub].y};
+        const uint32_t hv[2] = {cur.vh[sub].x, cur.vh[sub].y};
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        float f[16];
-        if (kValComb) {
+        for (int e = 0; e < 2; ++e) {
+          float f[16];
           const uint32_t lv = e ? cur.vl[sub].y : cur.vl[sub].x;
           unpack_combined(hv[e], lv, f);
-        } else {
-          unpack_plain(hv[e], f);
-        }
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          acc[16 * e + q] = fmaf(w, f[q], acc[16 * e + q]);
+          for (int q = 0; q < 16; ++q) acc[16 * e + q] = fmaf(w, f[q], acc[16 * e + q]);
         }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
       }
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      // Two value steps at a time: byte k of the two tokens' rows goes into
+      // the low bytes of a packed fp16 pair, and a 2-bit field masked in
+      // place is an fp16 subnormal code * 4^i * 2^-24 (exact).  One packed
+      // dot product then adds w_a * code_a + w_b * code_b in fp32; the
+      // weights w = p * s are rounded to fp16.  2^24 * 4^-i is applied in
+      // the epilogue.
+#pragma unroll
+      for (int sub = 0; sub < kSubs; sub += 2) {
+        float w2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float pp = ptile[(sub + u) * kSlots + vslot];   // 0 for tokens past the end
+          // rows past the end hold arbitrary bytes: zero their metadata
+          const uint32_t meta = (t0 + (sub + u) * kSlots + vslot < end) ? cur.vm[sub + u] : 0u;
+          const float vs = f16_to_f32(meta & 0xffffu), vz = f16_to_f32(meta >> 16);
+          w2[u] = pp * vs;
+          zs = kQ4 ? fmaf(pp, fmaf(1.5f, vs, vz), zs)    // bucket centre + zero
+                   : fmaf(pp, vz, zs);
+        }
+        const half2_t wp = {static_cast<_Float16>(w2[0]), static_cast<_Float16>(w2[1])};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t ra = e ? cur.vh[sub].y : cur.vh[sub].x;
+          const uint32_t rb = e ? cur.vh[sub + 1].y : cur.vh[sub + 1].x;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            // bytes: [ra.k, 0, rb.k, 0]
+            const uint32_t pr = __builtin_amdgcn_perm(rb, ra, 0x0C000C00u | ((4u + k) << 16) | k);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t m = pr & (0x00030003u << (2 * i));
+              acc[16 * e + 4 * i + k] =
+                  __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, m), wp, acc[16 * e + 4 * i + k], false);
+            }
+          }
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __syncthreads();
   };
@@ -638,10 +671,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   if (lane < kNJ) {
 #pragma unroll
     for (int c = 0; c < 32; ++c)
-      // constant factors kept out of the token loop: the fp8 unit, the high
-      // plane's weight 4, and the x4 of fields left in bits 2-3 of a byte
+      // constant factors kept out of the token loop: the fp8 unit (tau = 0),
+      // or the subnormal scale 2^24 * 4^-i; the high plane's weight 4
       part[kPartialPad + kGroup * lane + 16 * (c / 16) + pos_channel(c % 16)] =
-          fmaf(acc[c], inv_unit * (kValComb ? 1.0f : plain_factor(c % 16)) * ((kQ4 && !kValComb) ? 4.0f : 1.0f), zs);
+          fmaf(acc[c], kValComb ? inv_unit : dot2_factor(c % 16) * (kQ4 ? 4.0f : 1.0f), zs);
   }
   if (lane == 0) {
     part[0] = m;
