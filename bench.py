@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--tau-sweep", action="store_true",
                     help="time the workload at every tau of its sweep (one prefill)")
     ap.add_argument("--num-splits", type=int, default=0, help="splits per (sequence, head); 0 = auto")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each timed step as one captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-samples", type=int, default=8, help="(cell, sequence) oracle samples")
     ap.add_argument("--report", default=None, help="also write the JSON result to this file")
@@ -68,7 +70,7 @@ class Bench:
         self.kinds, self.taus = kinds, taus
         dev = torch.device("cuda", 0)
         self.dev = dev
-        self.steps_per_point = args.warmup + args.steps + 2
+        self.steps_per_point = args.warmup + args.steps + 2   # + per-kernel pass + counters pass
         extra = w.append_tokens * self.steps_per_point * n_points
         t0 = time.time()
         st = runner.CacheState(w, dev, kinds, taus, extra_tokens=extra)
@@ -91,6 +93,9 @@ class Bench:
         self.lens_dev = [torch.from_numpy((self.lens0 + s * w.append_tokens).astype(np.int32)).to(dev)
                          for s in range(total_steps + 1)]
         self.out = torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=dev)
+        self.lens_app_buf = torch.empty_like(self.lens_dev[0])
+        self.lens_dec_buf = torch.empty_like(self.lens_dev[0])
+        self.graph = None
         self.step_idx = 0
         log(f"[bench] setup {time.time() - t0:.1f} s")
 
@@ -104,21 +109,47 @@ class Bench:
     def lens_of(self, s):
         return self.lens0 + (s + 1) * self.w.append_tokens if self.w.append_tokens else self.lens0
 
-    def step(self, counters=None):
+    def launch_step(self, lens_app, lens_dec, sum_dec, counters=None):
+        """Enqueue one step: append to every stored cell, then decode every cell."""
         abi, st, w = self.abi, self.st, self.w
-        s = self.step_idx
         if w.append_tokens:
-            app = abi.make_batch(self.lens_dev[s], st.block_tables, st.max_seq_len)
+            app = abi.make_batch(lens_app, st.block_tables, st.max_seq_len)
             for c in st.stored:
                 k, v = self.new_kv[c]
                 abi.loopkv_append(st.plan, st.cells, c[0], c[1], app, w.append_tokens, k, v)
-        lens_now = self.lens_of(s) if w.append_tokens else self.lens0
-        bt = st.batch(self.lens_dev[s + 1] if w.append_tokens else self.lens_dev[0],
-                      sum_seq_lens=int(lens_now.sum()))
+        bt = st.batch(lens_dec, sum_seq_lens=sum_dec)
         o = abi.make_opts(st.workspace, counters=counters, num_splits=self.args.num_splits)
         for (r, l) in self.order:
             abi.loopkv_decode(st.plan, st.cells, r, l, bt, self.queries[(r, l)], self.out, o)
+
+    def step_lens(self, s):
+        """(lengths before the append, lengths attended) device tensors of step s."""
+        if self.w.append_tokens:
+            return self.lens_dev[s], self.lens_dev[s + 1]
+        return self.lens_dev[0], self.lens_dev[0]
+
+    def step(self, counters=None, eager=False):
+        s = self.step_idx
+        if self.graph is not None and counters is None and not eager:
+            # the captured step reads its lengths from two fixed buffers
+            la, ld = self.step_lens(s)
+            self.lens_app_buf.copy_(la)
+            self.lens_dec_buf.copy_(ld)
+            self.graph.replay()
+        else:
+            la, ld = self.step_lens(s)
+            self.launch_step(la, ld, int(self.lens_of(s).sum()), counters)
         self.step_idx += 1
+
+    def capture(self):
+        """Record one step (all appends and decodes) as a HIP graph."""
+        torch = self.torch
+        self.graph = None
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.launch_step(self.lens_app_buf, self.lens_dec_buf, int(self.lens_of(self.step_idx).sum()))
+        torch.cuda.synchronize()
+        self.graph = g
 
     def src_kind(self, r, l):
         R = self.w.loops
@@ -139,9 +170,12 @@ class Bench:
     def run_point(self):
         """Warmup, timed steps, a per-kernel pass and a counters pass."""
         torch, abi, args, w = self.torch, self.abi, self.args, self.w
+        self.graph = None
         for _ in range(args.warmup):
             self.step()
         torch.cuda.synchronize()
+        if args.graph:
+            self.capture()
         first = self.step_idx
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record()
@@ -156,7 +190,7 @@ class Bench:
         for c in (abi.KERNEL_SPLIT, abi.KERNEL_MERGE, abi.KERNEL_APPEND):
             abi.loopkv_profile_collect(c)
         prof_step = self.step_idx
-        self.step()
+        self.step(eager=True)
         torch.cuda.synchronize()
         kst = {name: abi.loopkv_profile_collect(c) for name, c in
                (("split", abi.KERNEL_SPLIT), ("merge", abi.KERNEL_MERGE), ("append", abi.KERNEL_APPEND))}
@@ -354,7 +388,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "loops": w.loops, "layers": w.layers,
                    "heads": w.heads, "head_dim": w.head_dim, "page": w.page,
                    "context": primary["context"], "tau": primary["tau"],
-                   "append_tokens_per_step": w.append_tokens},
+                   "append_tokens_per_step": w.append_tokens,
+                   "step_launch": "hip_graph" if args.graph else "eager"},
         "hbm_gbs_required": primary["hbm_gbs_required"],
         "hbm_frac_required": primary["hbm_gbs_required"] / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": sp["achieved_gbs"],

@@ -138,6 +138,62 @@ def test_small_tau_candidate_spill(tau):
             assert s["flagged"] > 0
 
 
+def test_graph_replay_matches_eager():
+    """Appends and decodes captured in one HIP graph give, on every replay,
+    the same bytes as the same calls made eagerly (eager work and
+    synchronizations run between the replays)."""
+    w = wl.Workload("graph", 180, batch=3, loops=2, layers=2, heads=4, head_dim=128, page=16,
+                    ctx=700, heavy_frac=0.01)
+    kinds, taus = [[Q4, Q2], [Q4, Q4]], [[0.01, 0.01], [0.0, math.inf]]
+    n_steps = 4
+    st_e = runner.CacheState(w, DEV, kinds, taus, extra_tokens=n_steps)
+    st_g = runner.CacheState(w, DEV, kinds, taus, extra_tokens=n_steps)
+    for st in (st_e, st_g):
+        for c in st.stored:
+            st.pools[c].zero_()     # unwritten bytes compare equal too
+        st.prefill()
+    cells = [(r, l) for r in range(2) for l in range(2)]
+    qs = {c: wl.cell_query(w, st_e.cell_index(*c), DEV)[1] for c in cells}
+    new = {c: wl.append_kv(w, st_e.cell_index(*c), 0, 1, DEV) for c in st_e.stored}
+    lens0 = torch.from_numpy(st_e.lens0.astype(np.int32)).to(DEV)
+
+    def run(st, lens_app, lens_dec, outs, masks):
+        app = abi.make_batch(lens_app, st.block_tables, st.max_seq_len)
+        for c in st.stored:
+            abi.loopkv_append(st.plan, st.cells, c[0], c[1], app, 1, *new[c])
+        for i, (r, l) in enumerate(cells):
+            st.decode(r, l, qs[(r, l)], outs[i], mask=masks[i], lens=lens_dec, sum_seq_lens=0)
+
+    def buffers(st):
+        return ([torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=DEV) for _ in cells],
+                [st.new_mask() for _ in cells])
+
+    la = torch.empty_like(lens0)
+    ld = torch.empty_like(lens0)
+    outs_g, masks_g = buffers(st_g)
+    la.copy_(lens0)
+    ld.copy_(lens0 + 1)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(st_g, la, ld, outs_g, masks_g)
+    torch.cuda.synchronize()
+    for step in range(n_steps):
+        outs_e, masks_e = buffers(st_e)
+        run(st_e, lens0 + step, lens0 + step + 1, outs_e, masks_e)
+        torch.cuda.synchronize()
+        la.copy_(lens0 + step)
+        ld.copy_(lens0 + step + 1)
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(len(cells)):
+            assert torch.equal(outs_g[i].view(torch.int32), outs_e[i].view(torch.int32)), (step, cells[i])
+            assert torch.equal(masks_g[i], masks_e[i]), (step, cells[i])
+        for c in st_e.stored:
+            assert torch.equal(st_g.pools[c], st_e.pools[c]), (step, c)
+        say(f"  replay {step}: {len(cells)} cells bit-identical to eager")
+
+
 def test_decode_is_deterministic():
     w = wl.Workload("determ", 150, batch=2, loops=1, layers=1, heads=4, head_dim=128, page=32,
                     ctx=5000, heavy_frac=0.01)
