@@ -42,9 +42,35 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-samples", type=int, default=8, help="(cell, sequence) oracle samples")
     ap.add_argument("--report", default=None, help="also write the JSON result to this file")
+    ap.add_argument("--probe-sizes", action="store_true",
+                    help="only print the read probe's bandwidth at several launch sizes and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="GIB",
                     help="only run 3 plain device copies of GIB GiB (counter calibration) and exit")
     return ap.parse_args()
+
+
+def probe_sizes():
+    """Read-probe bandwidth per launch size (how much one launch of a given
+    size can stream), one JSON line per size."""
+    import torch
+    from loop_aware_quantized_amd import abi
+    big = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
+    for mb in (256, 512, 805, 1074, 2048, 4096, 8192):
+        n = mb << 20
+        reps = max(3, min(50, (8 << 30) // n))
+        abi.loopkv_read_probe(big[:n])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            off = (r * n) % ((8 << 30) - n + 1)
+            off -= off % 4096
+            abi.loopkv_read_probe(big[off:off + n])    # a different window each time
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        print(json.dumps({"probe_mb": mb, "us_per_launch": round(us, 1),
+                          "tb_per_s": round(n / (us * 1e-6) / 1e12, 3)}), flush=True)
 
 
 def copy_probe(gib):
@@ -328,6 +354,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.probe_sizes:
+        probe_sizes()
         return
     import torch
     from loop_aware_quantized_amd import abi

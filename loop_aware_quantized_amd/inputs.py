@@ -42,7 +42,7 @@ class Workload:
     shuffle_pages: bool = False
     heavy_frac: float = 0.01      # Bernoulli fraction of heavy tokens
     heavy_count: int | None = None  # exact heavy tokens per (sequence, head)
-    plan: str = "random"          # "tiny" | "random" | "lean"
+    plan: str = "random"          # "tiny" | "random" | "lean" | "kivi4"
     taus: tuple = (0.01,)         # "random": per-cell draw; else one tau for all cells
     append_tokens: int = 0        # tokens appended per stored cell in one step
     tau_sweep: tuple = field(default=())
@@ -67,6 +67,10 @@ WORKLOADS = {
     "ragged-16k": Workload("ragged-16k", 3, batch=64, loops=4, layers=24, heads=16,
                            head_dim=128, page=16, ctx=16384, ctx_min=512, shuffle_pages=True,
                            heavy_frac=0.005, plan="random", taus=(0.005,)),
+    # KIVI-4-style baseline on the lean-16k shape and data: every cell stored
+    # at 4 bits, no reuse, tau = 0 (every low plane read)
+    "kivi4-16k": Workload("kivi4-16k", 2, batch=32, loops=4, layers=24, heads=16, head_dim=128,
+                          page=32, ctx=16384, plan="kivi4", taus=(0.0,), append_tokens=1),
     # Ouro-2.6B-like: 4 loops x 48 layers, batch 16, 32K context, tau sweep
     "ouro2.6b-32k": Workload("ouro2.6b-32k", 4, batch=16, loops=4, layers=48, heads=16,
                              head_dim=128, page=32, ctx=32768, plan="lean", taus=(0.01,),
@@ -124,6 +128,8 @@ def make_plan(w: Workload):
             q4, q2, ru = (c * mult for c in _LEAN_COUNTS_24[r])
             row = np.array([KIND_Q4] * q4 + [KIND_Q2] * q2 + [KIND_REUSE] * ru)
             kinds[r] = row[rng.permutation(L)]
+    elif w.plan == "kivi4":
+        kinds[:] = KIND_Q4
     else:
         raise ValueError(w.plan)
     if w.plan == "random" and len(w.taus) > 1:

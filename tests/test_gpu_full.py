@@ -113,3 +113,8 @@ def test_full_ragged_16k():
 def test_full_ouro26b_32k_tau_sweep():
     w = wl.WORKLOADS["ouro2.6b-32k"]
     _run(w, seqs=[2], tau_sweep=w.tau_sweep)
+
+
+def test_full_kivi4_16k_dense():
+    # same shape and data as lean-16k, every cell 4-bit with tau = 0
+    _run(wl.WORKLOADS["kivi4-16k"], seqs=[0, 31], append=True)
