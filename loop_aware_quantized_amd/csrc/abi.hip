@@ -455,6 +455,7 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
   a.max_pages = batch->max_pages;
   a.S = sp.S;
   a.split_len = sp.len;
+  a.graded_priority = static_cast<int64_t>(sp.S) * plan->H * batch->batch <= static_cast<int64_t>(cu_count()) * 12;
   a.mask_words = (batch->max_seq_len + 31) / 32;
   a.sm_scale = opts->sm_scale;
   a.log_tau = (mode == lkv::kModeSparse) ? std::log(tau) : 0.0f;

@@ -41,6 +41,7 @@ struct DecodeArgs {
   unsigned long long* counters;      // optional [2]
   int64_t num_pages;
   int32_t H, max_pages, S, split_len, mask_words;
+  int32_t graded_priority;           // 1: one round of waves, see decode_split_kernel
   float sm_scale;
   float log_tau;                     // ln(tau) for the candidate / flag test
   CellLayout lay;

@@ -138,6 +138,25 @@ def test_small_tau_candidate_spill(tau):
             assert s["flagged"] > 0
 
 
+def test_near_uniform_batch_vs_one_split():
+    """16 x 16 (sequence, head) pairs of near-equal length in the automatic
+    split layout: every mode matches the oracle, and the outputs match the
+    one-split-per-pair layout's."""
+    w = wl.Workload("ranked", 190, batch=16, loops=1, layers=3, heads=16, head_dim=128, page=32,
+                    ctx=6000, heavy_frac=0.01)
+    lens = [6000 - 7 * i for i in range(16)]
+    st = runner.CacheState(w, DEV, [[Q4, Q2, Q4]], [[0.01, 0.01, 0.0]], lengths=lens)
+    seqs = [0, 15]
+    kept = st.prefill({c: set(seqs) for c in st.stored})
+    for l in range(3):
+        q, out, mask, _ = _decode(st, 0, l)
+        s = compare_decode(st, 0, l, q, out, mask, kept[(0, l)], seqs)
+        q1, out1, mask1, _ = _decode(st, 0, l, num_splits=1, q=q)
+        rel = float((out - out1).abs().max() / out1.abs().max())
+        say(f"  layer {l}: rel err {s['rel']:.2e} flagged {s['flagged']}; vs one split {rel:.2e}")
+        assert rel < 1e-3
+
+
 def test_graph_replay_matches_eager():
     """Appends and decodes captured in one HIP graph give, on every replay,
     the same bytes as the same calls made eagerly (eager work and
