@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-samples", type=int, default=8, help="(cell, sequence) oracle samples")
     ap.add_argument("--report", default=None, help="also write the JSON result to this file")
+    ap.add_argument("--planner", action="store_true",
+                    help="only time the offline plan search (host) and exit")
     ap.add_argument("--probe-sizes", action="store_true",
                     help="only print the read probe's bandwidth at several launch sizes and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="GIB",
@@ -71,6 +73,27 @@ def probe_sizes():
         us = e0.elapsed_time(e1) * 1e3 / reps
         print(json.dumps({"probe_mb": mb, "us_per_launch": round(us, 1),
                           "tb_per_s": round(n / (us * 1e-6) / 1e12, 3)}), flush=True)
+
+
+def planner_report():
+    """Time the offline plan search on the synthetic damage tables of the
+    4 x 24 and 4 x 48 workloads; one JSON line each."""
+    from loop_aware_quantized_amd import abi
+    from loop_aware_quantized_amd import inputs as wl
+    for name in ("planned-16k", "ouro2.6b-32k"):
+        w = wl.WORKLOADS[name]
+        d = wl.synthetic_damage(w)
+        db, sb = wl.planner_budgets(w)
+        reps, t0 = 5, time.perf_counter()
+        for _ in range(reps):
+            kinds, (reads, store, dmg) = abi.loopkv_plan_optimize(d, db, sb)
+        ms = (time.perf_counter() - t0) * 1e3 / reps
+        print(json.dumps({"planner": name, "cells": w.loops * w.layers, "ms": round(ms, 2),
+                          "damage_budget": db, "storage_budget_units": sb, "reads_units": reads,
+                          "storage_units": store, "damage": dmg,
+                          "kinds": {k: int((kinds == v).sum()) for k, v in
+                                    (("q4", wl.KIND_Q4), ("q2", wl.KIND_Q2), ("reuse", wl.KIND_REUSE))}}),
+              flush=True)
 
 
 def copy_probe(gib):
@@ -357,6 +380,9 @@ def main():
         return
     if args.probe_sizes:
         probe_sizes()
+        return
+    if args.planner:
+        planner_report()
         return
     import torch
     from loop_aware_quantized_amd import abi

@@ -211,6 +211,35 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells,
                   const loopkv_decode_opts* opts, void* stream);
 
 /*
+ * loopkv_plan_optimize -- offline plan search: the kind of every cell that
+ * minimizes decode reads under a damage budget and a storage budget.
+ * Source: LoopKV abstract -- single-cell damages add up to the model's
+ * damage; a one-time offline profile chooses 4-bit storage, 2-bit storage
+ * or reuse of the final loop's KV per cell; the planner minimizes reads
+ * under budgets for predicted damage and storage.
+ * damage: host [R][L][4] doubles per cell (loop-major): predicted damage
+ *   when the cell is stored at 4 bits, at 2 bits, when it reuses a 4-bit
+ *   final-loop cell, when it reuses a 2-bit one (the reuse entries of loop
+ *   R-1 are ignored).  Finite, >= 0.
+ * Costs per token-head in 32-byte units (head_dim 128): reads 4 (a 4-bit
+ *   source: both key planes, high value plane, metadata) or 3 (2-bit);
+ *   a reuse cell reads its source's format.  Storage 5 (4-bit: four planes
+ *   + metadata), 3 (2-bit), 0 (reuse).  Low-plane fetches of flagged tokens
+ *   are not counted.
+ * Result: among plans with total damage <= damage_budget and total storage
+ *   <= storage_budget, the one with least reads, then least damage, then
+ *   least storage.  kinds: host out [R][L] LOOPKV_CELL_* (reuse never in
+ *   loop R-1).  totals: host out [3] (reads, storage, damage), may be NULL.
+ * The search is exact (dynamic program over layers; O(L * (20R L)^2 / 3)
+ *   time for R = 4).
+ * Errors: LOOPKV_E_INVAL (R not in 1..8, L not in 1..4096, NULL pointers,
+ *   negative / non-finite inputs, instance too large), LOOPKV_E_PLAN (no
+ *   plan meets both budgets).
+ */
+int loopkv_plan_optimize(int32_t R, int32_t L, const double* damage, double damage_budget,
+                         int64_t storage_budget, uint8_t* kinds, double* totals);
+
+/*
  * Measurement hook (not an operation of the method; used by benchmarks to
  * time kernels live).  While enabled, every kernel launch this library makes
  * is bracketed by a pair of HIP events recorded on the launch's own stream.

@@ -43,6 +43,7 @@ _SIGNATURES = {
     "loopkv_profile_enable": (c_int, [c_int]),
     "loopkv_profile_collect": (c_int, [c_int, POINTER(c_int64), POINTER(ctypes.c_double)]),
     "loopkv_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
+    "loopkv_plan_optimize": (c_int, [c_int32, c_int32, c_void_p, ctypes.c_double, c_int64, c_void_p, c_void_p]),
 }
 
 KERNEL_SPLIT = 0
@@ -253,3 +254,23 @@ def loopkv_read_probe(buf, sink=None, stream=None) -> int:
     """Stream-read a device tensor (bandwidth probe)."""
     return _check(lib().loopkv_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                           _stream_handle(stream)))
+
+
+def loopkv_plan_optimize(damage, damage_budget: float, storage_budget: int):
+    """Least-reads plan under damage and storage budgets.
+
+    damage: float64 array [R][L][4] (4-bit, 2-bit, reuse of a 4-bit final
+    cell, reuse of a 2-bit final cell).  Returns (kinds int array [R][L],
+    (reads, storage, damage) totals); raises LoopKVError (code E_PLAN) when
+    no plan meets both budgets.
+    """
+    import numpy as np
+    d = np.ascontiguousarray(damage, dtype=np.float64)
+    if d.ndim != 3 or d.shape[2] != 4:
+        raise ValueError("damage must be [R][L][4]")
+    R, L = d.shape[0], d.shape[1]
+    kinds = np.zeros((R, L), np.uint8)
+    totals = np.zeros(3, np.float64)
+    _check(lib().loopkv_plan_optimize(R, L, d.ctypes.data, float(damage_budget), int(storage_budget),
+                                      kinds.ctypes.data, totals.ctypes.data))
+    return kinds.astype(np.int64), (int(totals[0]), int(totals[1]), float(totals[2]))

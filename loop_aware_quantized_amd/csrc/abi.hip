@@ -29,8 +29,14 @@ struct loopkv_plan {
 };
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
+
+namespace lkv {
+void set_last_error(const char* msg) { g_err = msg; }
+}  // namespace lkv
+
+namespace {
 
 int fail(int code, const std::string& msg) {
   g_err = msg;

@@ -24,7 +24,7 @@ import numpy as np
 KIND_Q4, KIND_Q2, KIND_REUSE = 0, 1, 2
 
 # purposes of seeded streams
-_P_PLAN, _P_TAU, _P_LENS, _P_PAGES, _P_KV, _P_APPEND = range(6)
+_P_PLAN, _P_TAU, _P_LENS, _P_PAGES, _P_KV, _P_APPEND, _P_DAMAGE = range(7)
 
 
 @dataclass(frozen=True)
@@ -42,7 +42,7 @@ class Workload:
     shuffle_pages: bool = False
     heavy_frac: float = 0.01      # Bernoulli fraction of heavy tokens
     heavy_count: int | None = None  # exact heavy tokens per (sequence, head)
-    plan: str = "random"          # "tiny" | "random" | "lean" | "kivi4"
+    plan: str = "random"          # "tiny" | "random" | "lean" | "kivi4" | "planned"
     taus: tuple = (0.01,)         # "random": per-cell draw; else one tau for all cells
     append_tokens: int = 0        # tokens appended per stored cell in one step
     tau_sweep: tuple = field(default=())
@@ -71,6 +71,11 @@ WORKLOADS = {
     # at 4 bits, no reuse, tau = 0 (every low plane read)
     "kivi4-16k": Workload("kivi4-16k", 2, batch=32, loops=4, layers=24, heads=16, head_dim=128,
                           page=32, ctx=16384, plan="kivi4", taus=(0.0,), append_tokens=1),
+    # lean-16k's shape and data with the plan found by the offline planner on
+    # a synthetic damage table (storage within 48.75% of all-4-bit, the lean
+    # plan's share; damage within half of the all-2-bit plan's)
+    "planned-16k": Workload("planned-16k", 2, batch=32, loops=4, layers=24, heads=16, head_dim=128,
+                            page=32, ctx=16384, plan="planned", taus=(0.01,), append_tokens=1),
     # Ouro-2.6B-like: 4 loops x 48 layers, batch 16, 32K context, tau sweep
     "ouro2.6b-32k": Workload("ouro2.6b-32k", 4, batch=16, loops=4, layers=48, heads=16,
                              head_dim=128, page=32, ctx=32768, plan="lean", taus=(0.01,),
@@ -130,6 +135,9 @@ def make_plan(w: Workload):
             kinds[r] = row[rng.permutation(L)]
     elif w.plan == "kivi4":
         kinds[:] = KIND_Q4
+    elif w.plan == "planned":
+        from . import abi
+        kinds, _ = abi.loopkv_plan_optimize(synthetic_damage(w), *planner_budgets(w))
     else:
         raise ValueError(w.plan)
     if w.plan == "random" and len(w.taus) > 1:
@@ -137,6 +145,39 @@ def make_plan(w: Workload):
     else:
         taus = np.full((R, L), float(w.taus[0]))
     return kinds, taus
+
+
+def synthetic_damage(w: Workload) -> np.ndarray:
+    """Seeded stand-in for a per-cell damage profile, float64 [R][L][4]:
+    (4-bit, 2-bit, reuse of a 4-bit final cell, reuse of a 2-bit one).
+
+    No profile of a real model exists here (it needs Ouro weights and data);
+    the table only has the properties the LoopKV abstract states: damage
+    varies across (loop, layer) cells, and sharing damage varies by cell
+    with later loops tolerating sharing better.  A cell's quantization
+    sensitivity s is log-normal (sigma 0.5); 2-bit damage is s and 4-bit
+    damage s/25 (a 4-bit step is a fifth of a 2-bit one; squared error goes
+    with the step squared).  Sharing damage is log-normal (sigma 0.5) times
+    (R-1-r)/(R-1); a reuse cell also sees its source's quantization.
+    """
+    R, L = w.loops, w.layers
+    rng = np_rng(w, _P_DAMAGE)
+    sens = np.exp(rng.normal(0.0, 0.5, (R, L)))
+    share = np.exp(rng.normal(0.0, 0.5, (R, L))) * ((R - 1 - np.arange(R)) / max(R - 1, 1))[:, None]
+    d = np.empty((R, L, 4))
+    d[..., 0] = sens / 25.0
+    d[..., 1] = sens
+    d[..., 2] = share + sens / 25.0
+    d[..., 3] = share + sens
+    return d
+
+
+def planner_budgets(w: Workload):
+    """(damage budget, storage budget in 32-byte units per token-head) of a
+    planned workload: half the all-2-bit plan's damage, 48.75% of the
+    all-4-bit plan's storage (the share the memory-lean plan stores)."""
+    d = synthetic_damage(w)
+    return 0.5 * float(d[..., 1].sum()), int(0.4875 * 5 * w.loops * w.layers)
 
 
 def with_tau(taus, tau: float):

@@ -118,3 +118,8 @@ def test_full_ouro26b_32k_tau_sweep():
 def test_full_kivi4_16k_dense():
     # same shape and data as lean-16k, every cell 4-bit with tau = 0
     _run(wl.WORKLOADS["kivi4-16k"], seqs=[0, 31], append=True)
+
+
+def test_full_planned_16k():
+    # the offline planner's plan on the lean-16k shape and data
+    _run(wl.WORKLOADS["planned-16k"], seqs=[1, 30], append=True)
