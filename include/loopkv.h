@@ -240,6 +240,68 @@ int loopkv_plan_optimize(int32_t R, int32_t L, const double* damage, double dama
                          int64_t storage_budget, uint8_t* kinds, double* totals);
 
 /*
+ * ---- Joint vector quantization across loop steps (LoopVQ-style) ---------
+ * Source: "LoopVQ: Sub 1-bit KV Cache Quantization for Looped
+ * Transformers", abstract -- the KV cache of a looped model is redundant
+ * along the loop axis; codebooks code channels of several loop steps
+ * jointly, at 0.5 bit per element.
+ * Format of one layer (all R loops share it): for a token and head, channel
+ * group j (channels 4j..4j+3, j < D/4) has a joint vector of 4R numbers,
+ * loop r's channels at positions 4r..4r+3; its key (value) index is one
+ * byte naming the nearest of 256 codewords of group j's key (value)
+ * codebook.  R = 4 gives 8 bits per 16 elements = 0.5 bit per element.
+ * Codebook (one layer, keys or values): device fp16 [D/4][256][4R].
+ * Pool: device, head-major like the cell pools: head h of physical page p
+ *   at byte (h*num_pages + p) * 2*P*(D/4); inside, P key index rows of D/4
+ *   bytes, then P value index rows.
+ */
+typedef struct {
+  int32_t loops;       /* R, 2..4 */
+  int32_t heads;       /* H >= 1 */
+  int32_t head_dim;    /* D, 64 or 128 */
+  int32_t page;        /* P, 16, 32 or 64 */
+} loopkv_vq_dims;
+
+/* Bytes of one codebook, of a pool of num_pages pages, and of the decode
+ * workspace (no initial contents needed); 0 for invalid dims. */
+size_t loopkv_vq_codebook_bytes(const loopkv_vq_dims* dims);
+size_t loopkv_vq_pool_bytes(const loopkv_vq_dims* dims, int64_t num_pages);
+size_t loopkv_vq_workspace_bytes(const loopkv_vq_dims* dims, int32_t batch, int32_t max_seq_len);
+
+/*
+ * loopkv_vq_append -- code n_new new tokens of every sequence: each joint
+ * vector gets the index of its nearest codeword (squared Euclidean distance
+ * in fp32, ties to the lowest index).
+ * k_bf16, v_bf16: device [R][B][n_new][H][D] bfloat16, all loops' keys and
+ *   values of tokens seq_lens[b] .. seq_lens[b]+n_new-1, 8-byte aligned.
+ * codebook_k / codebook_v: device fp16 [D/4][256][4R], 8-byte aligned.
+ * Pages for all tokens < seq_lens[b] + n_new must be mapped.
+ * Errors: LOOPKV_E_INVAL (bad dims, NULL pointers, n_new < 1, misaligned
+ *   inputs, max_pages * P < max_seq_len), LOOPKV_E_HIP.
+ */
+int loopkv_vq_append(const loopkv_vq_dims* dims, void* pool, int64_t num_pages,
+                     const void* codebook_k, const void* codebook_v,
+                     const loopkv_batch* batch, int32_t n_new,
+                     const void* k_bf16, const void* v_bf16, void* stream);
+
+/*
+ * loopkv_vq_decode -- one decode step of loop `loop` over a layer's joint
+ * cache: keys and values are the loop's slices (positions 4*loop ..
+ * 4*loop+3) of the chosen codewords; o = softmax(sm_scale * q.K^) V^.
+ * q_bf16: device [B][H][D] bfloat16 (8-byte aligned); out: device fp32
+ * [B][H][D].  A sequence of length 0 produces zeros.  Value weights are
+ * accumulated with float atomics, so the last bits of out may differ
+ * between runs.
+ * Errors: LOOPKV_E_INVAL, LOOPKV_E_CAPACITY (workspace too small),
+ *   LOOPKV_E_HIP.
+ */
+int loopkv_vq_decode(const loopkv_vq_dims* dims, const void* pool, int64_t num_pages,
+                     const void* codebook_k, const void* codebook_v, int loop,
+                     const loopkv_batch* batch, const void* q_bf16, float* out,
+                     float sm_scale, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
  * Measurement hook (not an operation of the method; used by benchmarks to
  * time kernels live).  While enabled, every kernel launch this library makes
  * is bracketed by a pair of HIP events recorded on the launch's own stream.

@@ -44,6 +44,13 @@ _SIGNATURES = {
     "loopkv_profile_collect": (c_int, [c_int, POINTER(c_int64), POINTER(ctypes.c_double)]),
     "loopkv_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "loopkv_plan_optimize": (c_int, [c_int32, c_int32, c_void_p, ctypes.c_double, c_int64, c_void_p, c_void_p]),
+    "loopkv_vq_codebook_bytes": (c_size_t, [c_void_p]),
+    "loopkv_vq_pool_bytes": (c_size_t, [c_void_p, c_int64]),
+    "loopkv_vq_workspace_bytes": (c_size_t, [c_void_p, c_int32, c_int32]),
+    "loopkv_vq_append": (c_int, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                 c_void_p, c_void_p]),
+    "loopkv_vq_decode": (c_int, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int, c_void_p, c_void_p,
+                                 c_void_p, c_float, c_void_p, c_size_t, c_void_p]),
 }
 
 KERNEL_SPLIT = 0
@@ -68,6 +75,11 @@ class DecodeOpts(ctypes.Structure):
     """loopkv_decode_opts"""
     _fields_ = [("sm_scale", c_float), ("num_splits", c_int32), ("workspace", c_void_p),
                 ("workspace_bytes", c_size_t), ("mask_bits", c_void_p), ("counters", c_void_p)]
+
+
+class VqDims(ctypes.Structure):
+    """loopkv_vq_dims"""
+    _fields_ = [("loops", c_int32), ("heads", c_int32), ("head_dim", c_int32), ("page", c_int32)]
 
 
 class LoopKVError(RuntimeError):
@@ -274,3 +286,40 @@ def loopkv_plan_optimize(damage, damage_budget: float, storage_budget: int):
     _check(lib().loopkv_plan_optimize(R, L, d.ctypes.data, float(damage_budget), int(storage_budget),
                                       kinds.ctypes.data, totals.ctypes.data))
     return kinds.astype(np.int64), (int(totals[0]), int(totals[1]), float(totals[2]))
+
+
+# ----------------------------------------------------------------------------
+# joint vector quantization across loop steps
+# ----------------------------------------------------------------------------
+
+def vq_dims(loops: int, heads: int, head_dim: int, page: int) -> VqDims:
+    return VqDims(loops, heads, head_dim, page)
+
+
+def vq_codebook_bytes(dims: VqDims) -> int:
+    return lib().loopkv_vq_codebook_bytes(ctypes.byref(dims))
+
+
+def vq_pool_bytes(dims: VqDims, num_pages: int) -> int:
+    return lib().loopkv_vq_pool_bytes(ctypes.byref(dims), num_pages)
+
+
+def vq_workspace_bytes(dims: VqDims, batch: int, max_seq_len: int) -> int:
+    return lib().loopkv_vq_workspace_bytes(ctypes.byref(dims), batch, max_seq_len)
+
+
+def loopkv_vq_append(dims: VqDims, pool, num_pages: int, codebook_k, codebook_v, batch: Batch, n_new: int,
+                     k, v, stream=None) -> int:
+    """Code n_new tokens of every sequence (k, v: [R][B][n_new][H][D] bf16)."""
+    return _check(lib().loopkv_vq_append(ctypes.byref(dims), _ptr(pool), num_pages, _ptr(codebook_k),
+                                         _ptr(codebook_v), ctypes.byref(batch), n_new, _ptr(k), _ptr(v),
+                                         _stream_handle(stream)))
+
+
+def loopkv_vq_decode(dims: VqDims, pool, num_pages: int, codebook_k, codebook_v, loop: int, batch: Batch,
+                     q, out, workspace, sm_scale: float = 1.0, stream=None) -> int:
+    """Decode step of loop `loop` over a layer's joint cache; writes fp32 out [B][H][D]."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return _check(lib().loopkv_vq_decode(ctypes.byref(dims), _ptr(pool), num_pages, _ptr(codebook_k),
+                                         _ptr(codebook_v), loop, ctypes.byref(batch), _ptr(q), _ptr(out),
+                                         float(sm_scale), _ptr(workspace), nbytes, _stream_handle(stream)))

@@ -472,4 +472,154 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
   return LOOPKV_OK;
 }
 
+// ---- joint vector quantization across loop steps -------------------------
+
+namespace {
+
+const char* vq_dims_error(const loopkv_vq_dims* d) {
+  if (!d) return "vq: NULL dims";
+  if (d->loops < 2 || d->loops > 4) return "vq: loops must be 2, 3 or 4";
+  if (d->heads < 1) return "vq: heads must be >= 1";
+  if (d->head_dim != 64 && d->head_dim != 128) return "vq: head_dim must be 64 or 128";
+  if (d->page != 16 && d->page != 32 && d->page != 64) return "vq: page must be 16, 32 or 64";
+  return nullptr;
+}
+
+int64_t vq_head_block(const loopkv_vq_dims* d) {
+  return static_cast<int64_t>(2) * d->page * (d->head_dim / lkv::kVqSub);
+}
+
+struct VqSplits {
+  int S, len;
+};
+
+// Splits of 2048 tokens when that still gives four blocks per compute unit
+// (two are resident at a time), else of 1024.
+VqSplits vq_splits(int64_t batch, int64_t heads, int t_max) {
+  const int64_t tm = std::max<int64_t>(t_max, 1);
+  int64_t len = lkv::kVqSplitMax;
+  if (batch * heads * ((tm + len - 1) / len) < static_cast<int64_t>(cu_count()) * 4) len = lkv::kVqSplitMax / 2;
+  return {static_cast<int>((tm + len - 1) / len), static_cast<int>(len)};
+}
+
+}  // namespace
+
+size_t loopkv_vq_codebook_bytes(const loopkv_vq_dims* d) {
+  if (vq_dims_error(d)) return 0;
+  return static_cast<size_t>(d->head_dim / lkv::kVqSub) * lkv::kVqCodes * lkv::kVqSub * d->loops * 2;
+}
+
+size_t loopkv_vq_pool_bytes(const loopkv_vq_dims* d, int64_t num_pages) {
+  if (vq_dims_error(d) || num_pages < 0) return 0;
+  return static_cast<size_t>(d->heads) * num_pages * vq_head_block(d);
+}
+
+size_t loopkv_vq_workspace_bytes(const loopkv_vq_dims* d, int32_t batch, int32_t max_seq_len) {
+  if (vq_dims_error(d) || batch < 0 || max_seq_len < 0) return 0;
+  const int64_t s_max = (std::max<int64_t>(max_seq_len, 1) + lkv::kVqSplitMax / 2 - 1) / (lkv::kVqSplitMax / 2);
+  return static_cast<size_t>(round_up(static_cast<int64_t>(batch) * d->heads * s_max * (d->head_dim + lkv::kPartialPad) * 4, 256));
+}
+
+int loopkv_vq_append(const loopkv_vq_dims* d, void* pool, int64_t num_pages, const void* codebook_k,
+                     const void* codebook_v, const loopkv_batch* batch, int32_t n_new, const void* k_bf16,
+                     const void* v_bf16, void* stream) {
+  if (const char* e = vq_dims_error(d)) return fail(LOOPKV_E_INVAL, e);
+  if (!pool || !codebook_k || !codebook_v || !batch || !k_bf16 || !v_bf16)
+    return fail(LOOPKV_E_INVAL, "vq_append: NULL pointer");
+  if (n_new < 1) return fail(LOOPKV_E_INVAL, "vq_append: n_new must be >= 1");
+  if (num_pages < 1) return fail(LOOPKV_E_INVAL, "vq_append: num_pages must be >= 1");
+  if (batch->batch < 0 || batch->max_pages < 1 || !batch->seq_lens || !batch->block_tables)
+    return fail(LOOPKV_E_INVAL, "vq_append: bad batch");
+  if (static_cast<int64_t>(batch->max_pages) * d->page < batch->max_seq_len)
+    return fail(LOOPKV_E_INVAL, "vq_append: max_pages * page < max_seq_len");
+  if ((reinterpret_cast<uintptr_t>(k_bf16) | reinterpret_cast<uintptr_t>(v_bf16) |
+       reinterpret_cast<uintptr_t>(codebook_k) | reinterpret_cast<uintptr_t>(codebook_v)) % 8 != 0)
+    return fail(LOOPKV_E_INVAL, "vq_append: inputs and codebooks must be 8-byte aligned");
+  if (batch->batch == 0) return LOOPKV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_enabled()) {
+    const int rc = debug_check(batch, d->page, num_pages, n_new, 0, s);
+    if (rc != LOOPKV_OK) return rc;
+  }
+  lkv::VqArgs a{};
+  a.pool = static_cast<uint8_t*>(pool);
+  a.cb_k = static_cast<const uint16_t*>(codebook_k);
+  a.cb_v = static_cast<const uint16_t*>(codebook_v);
+  a.seq_lens = batch->seq_lens;
+  a.block_tables = batch->block_tables;
+  a.k_in = static_cast<const uint16_t*>(k_bf16);
+  a.v_in = static_cast<const uint16_t*>(v_bf16);
+  a.num_pages = num_pages;
+  a.R = d->loops;
+  a.batch = batch->batch;
+  a.H = d->heads;
+  a.P = d->page;
+  a.max_pages = batch->max_pages;
+  a.n_new = n_new;
+  const hipError_t e = lkv::launch_vq_encode(a, d->head_dim, s);
+  if (e != hipSuccess) return fail_hip(e, "vq_append: kernel launch");
+  g_err.clear();
+  return LOOPKV_OK;
+}
+
+int loopkv_vq_decode(const loopkv_vq_dims* d, const void* pool, int64_t num_pages, const void* codebook_k,
+                     const void* codebook_v, int loop, const loopkv_batch* batch, const void* q_bf16, float* out,
+                     float sm_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (const char* e = vq_dims_error(d)) return fail(LOOPKV_E_INVAL, e);
+  if (loop < 0 || loop >= d->loops) return fail(LOOPKV_E_INVAL, "vq_decode: loop out of range");
+  if (!pool || !codebook_k || !codebook_v || !batch || !q_bf16 || !out || !workspace)
+    return fail(LOOPKV_E_INVAL, "vq_decode: NULL pointer");
+  if (num_pages < 1) return fail(LOOPKV_E_INVAL, "vq_decode: num_pages must be >= 1");
+  if (batch->batch < 0 || batch->max_pages < 1 || !batch->seq_lens || !batch->block_tables || batch->max_seq_len < 0)
+    return fail(LOOPKV_E_INVAL, "vq_decode: bad batch");
+  if (static_cast<int64_t>(batch->max_pages) * d->page < batch->max_seq_len)
+    return fail(LOOPKV_E_INVAL, "vq_decode: max_pages * page < max_seq_len");
+  if ((reinterpret_cast<uintptr_t>(q_bf16) | reinterpret_cast<uintptr_t>(codebook_k) |
+       reinterpret_cast<uintptr_t>(codebook_v)) % 8 != 0 || reinterpret_cast<uintptr_t>(pool) % 16 != 0)
+    return fail(LOOPKV_E_INVAL, "vq_decode: query / codebooks must be 8-byte and the pool 16-byte aligned");
+  if (workspace_bytes < loopkv_vq_workspace_bytes(d, batch->batch, batch->max_seq_len))
+    return fail(LOOPKV_E_CAPACITY, "vq_decode: workspace smaller than loopkv_vq_workspace_bytes");
+  if (batch->batch == 0) return LOOPKV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_enabled()) {
+    const int rc = debug_check(batch, d->page, num_pages, 0, 0, s);
+    if (rc != LOOPKV_OK) return rc;
+  }
+  const VqSplits sp = vq_splits(batch->batch, d->heads, batch->max_seq_len);
+  lkv::VqArgs a{};
+  a.pool = static_cast<uint8_t*>(const_cast<void*>(pool));
+  a.cb_k = static_cast<const uint16_t*>(codebook_k);
+  a.cb_v = static_cast<const uint16_t*>(codebook_v);
+  a.seq_lens = batch->seq_lens;
+  a.block_tables = batch->block_tables;
+  a.q = static_cast<const uint16_t*>(q_bf16);
+  a.partials = static_cast<float*>(workspace);
+  a.num_pages = num_pages;
+  a.R = d->loops;
+  a.batch = batch->batch;
+  a.H = d->heads;
+  a.P = d->page;
+  a.max_pages = batch->max_pages;
+  a.loop = loop;
+  a.S = sp.S;
+  a.split_len = sp.len;
+  a.sm_scale = sm_scale;
+  hipError_t e = lkv::launch_vq_split(a, d->head_dim, s);
+  if (e != hipSuccess) return fail_hip(e, "vq_decode: split kernel launch");
+  lkv::DecodeArgs m{};
+  m.seq_lens = batch->seq_lens;
+  m.block_tables = batch->block_tables;
+  m.out = out;
+  m.partials = static_cast<float*>(workspace);
+  m.H = d->heads;
+  m.max_pages = batch->max_pages;
+  m.S = sp.S;
+  m.split_len = sp.len;
+  m.lay = lkv::make_layout(lkv::kKindQ2, d->page, d->head_dim);
+  e = lkv::launch_merge_plain(m, batch->batch, s);
+  if (e != hipSuccess) return fail_hip(e, "vq_decode: merge kernel launch");
+  g_err.clear();
+  return LOOPKV_OK;
+}
+
 }  // extern "C"

@@ -738,6 +738,17 @@ hipError_t launch_d(const DecodeArgs& a, int batch, int mode, hipStream_t stream
 
 }  // namespace
 
+hipError_t launch_merge_plain(const DecodeArgs& a, int batch, hipStream_t stream) {
+  prof_mark(kClassMerge, 0, stream);
+  if (a.lay.D == 128)
+    hipLaunchKernelGGL((decode_merge_kernel<128, kKindQ2, kModePlain>), dim3(a.H, batch), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<64, kKindQ2, kModePlain>), dim3(a.H, batch), dim3(64), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  prof_mark(kClassMerge, 1, stream);
+  return e;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int batch, int mode, hipStream_t stream) {
   return a.lay.D == 128 ? launch_d<128>(a, batch, mode, stream) : launch_d<64>(a, batch, mode, stream);
 }

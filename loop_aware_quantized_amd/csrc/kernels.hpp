@@ -63,5 +63,30 @@ hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks,
                              hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int batch, int mode, hipStream_t stream);
+// log-sum-exp merge of plain partials only (no tau mask)
+hipError_t launch_merge_plain(const DecodeArgs& a, int batch, hipStream_t stream);
+
+// ---- joint vector quantization across loop steps (LoopVQ-style) ---------
+constexpr int kVqSub = 4;            // channels per loop in one joint vector
+constexpr int kVqCodes = 256;        // codewords per codebook (8-bit index)
+constexpr int kVqSplitMax = 2048;    // tokens per decode split (LDS scores)
+
+struct VqArgs {
+  uint8_t* pool;                     // [H][num_pages][2][P][D/4] indices (K rows, V rows)
+  const uint16_t* cb_k;              // [D/4][256][4R] fp16 codebook of the keys
+  const uint16_t* cb_v;              // same for the values
+  const int32_t* seq_lens;
+  const int32_t* block_tables;
+  const uint16_t* k_in;              // encode: [R][B][n_new][H][D] bf16
+  const uint16_t* v_in;
+  const uint16_t* q;                 // decode: [B][H][D] bf16
+  float* partials;                   // decode: [B][H][S][D + kPartialPad]
+  int64_t num_pages;
+  int32_t R, batch, H, P, max_pages, n_new, loop, S, split_len;
+  float sm_scale;
+};
+
+hipError_t launch_vq_encode(const VqArgs& a, int D, hipStream_t stream);
+hipError_t launch_vq_split(const VqArgs& a, int D, hipStream_t stream);
 
 }  // namespace lkv

@@ -295,3 +295,89 @@ def bf16_bits(t) -> np.ndarray:
     """bf16 torch tensor -> numpy uint16 bit patterns (host copy)."""
     import torch
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# joint vector quantization across loop steps (LoopVQ-style workloads)
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class VqWorkload:
+    name: str
+    wid: int
+    batch: int
+    loops: int
+    layers: int
+    heads: int
+    head_dim: int
+    page: int
+    ctx: int
+    append_tokens: int = 0
+    loop_noise: float = 0.25      # per-loop deviation from the shared vector
+
+    # the fields make_block_tables reads
+    ctx_min = None
+    shuffle_pages = False
+
+
+VQ_WORKLOADS = {
+    "loopvq-tiny": VqWorkload("loopvq-tiny", 10, batch=2, loops=4, layers=2, heads=2, head_dim=64, page=16,
+                              ctx=300),
+    # the lean-16k model shape and batch: 4 loops x 24 layers, 16 heads of 128,
+    # 32 sequences of 16K tokens, one token appended per step
+    "loopvq-16k": VqWorkload("loopvq-16k", 11, batch=32, loops=4, layers=24, heads=16, head_dim=128, page=32,
+                             ctx=16384, append_tokens=1),
+}
+
+
+def vq_codebooks(w: VqWorkload, layer: int, device):
+    """(keys, values) codebooks of one layer, fp16 [D/4][256][4R].
+
+    Codebook training is out of scope; the codewords are draws from the
+    same loop-redundant model as the data: a shared 4-vector per group plus
+    loop_noise * N(0, 1) per loop.
+    """
+    import torch
+    G, R = w.head_dim // 4, w.loops
+    out = []
+    for kv in range(2):
+        g = _gen(w, device, _P_KV, layer, 100 + kv)
+        base = torch.randn(G, 256, 1, 4, generator=g, device=device)
+        cw = base + w.loop_noise * torch.randn(G, 256, R, 4, generator=g, device=device)
+        out.append(cw.reshape(G, 256, 4 * R).to(torch.float16).contiguous())
+    return out[0], out[1]
+
+
+def vq_kv(w: VqWorkload, layer: int, b: int, t0: int, t1: int, device):
+    """Keys and values of tokens [t0, t1) of sequence b, all loops:
+    bf16 [R][1][t1 - t0][H][D] each (loop-redundant: shared + noise)."""
+    import torch
+    n = t1 - t0
+    out = []
+    for kv in range(2):
+        g = _gen(w, device, _P_KV, layer, 200 + kv, b, t0)
+        base = torch.randn(1, 1, n, w.heads, w.head_dim, generator=g, device=device)
+        x = base + w.loop_noise * torch.randn(w.loops, 1, n, w.heads, w.head_dim, generator=g, device=device)
+        out.append(x.to(torch.bfloat16).contiguous())
+    return out[0], out[1]
+
+
+def vq_append_kv(w: VqWorkload, layer: int, step: int, n_new: int, device):
+    """Keys and values of n_new appended tokens of every sequence: bf16 [R][B][n_new][H][D]."""
+    import torch
+    out = []
+    for kv in range(2):
+        g = _gen(w, device, _P_APPEND, layer, 300 + kv, step)
+        base = torch.randn(1, w.batch, n_new, w.heads, w.head_dim, generator=g, device=device)
+        x = base + w.loop_noise * torch.randn(w.loops, w.batch, n_new, w.heads, w.head_dim, generator=g,
+                                               device=device)
+        out.append(x.to(torch.bfloat16).contiguous())
+    return out[0], out[1]
+
+
+def vq_query(w: VqWorkload, layer: int, loop: int, device):
+    """bf16 [B][H][D] query of one (loop, layer): N(0, 1) / sqrt(D)."""
+    import torch
+    g = _gen(w, device, _P_KV, layer, 400 + loop)
+    q = torch.randn(w.batch, w.heads, w.head_dim, generator=g, device=device) / math.sqrt(w.head_dim)
+    return q.to(torch.bfloat16)

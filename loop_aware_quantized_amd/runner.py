@@ -135,3 +135,67 @@ def required_bytes_per_token_head(kind_src: int, head_dim: int) -> int:
     A flagged token adds its V low-plane row (D/4), counted separately.
     """
     return head_dim if kind_src == wl.KIND_Q4 else (3 * head_dim) // 4
+
+
+class VqState:
+    """Joint-code caches (one per layer) of a LoopVQ-style workload."""
+
+    def __init__(self, w: wl.VqWorkload, device, extra_tokens: int = 0, layers=None, lengths=None):
+        import torch
+        self.w = w
+        self.device = device
+        self.dims = abi.vq_dims(w.loops, w.heads, w.head_dim, w.page)
+        self.lens0 = np.full(w.batch, w.ctx, np.int32) if lengths is None else np.asarray(lengths, np.int32)
+        self.capacity = self.lens0.astype(np.int64) + extra_tokens
+        table, num_pages = wl.make_block_tables(w, self.capacity)
+        self.table_np = table
+        self.num_pages = num_pages
+        self.block_tables = torch.from_numpy(table).to(device)
+        self.max_seq_len = int(self.capacity.max())
+        self.layers = list(range(w.layers)) if layers is None else list(layers)
+        self.pools, self.codebooks = {}, {}
+        for l in self.layers:
+            self.pools[l] = torch.zeros(abi.vq_pool_bytes(self.dims, num_pages), dtype=torch.uint8, device=device)
+            self.codebooks[l] = wl.vq_codebooks(w, l, device)
+        self.workspace = torch.empty(abi.vq_workspace_bytes(self.dims, w.batch, self.max_seq_len),
+                                     dtype=torch.uint8, device=device)
+        self.lens = torch.from_numpy(self.lens0.astype(np.int32)).to(device)
+        self._zero = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def append(self, l: int, k, v, lens_before, table=None, max_seq_len=None):
+        table = self.block_tables if table is None else table
+        batch = abi.make_batch(lens_before, table, self.max_seq_len if max_seq_len is None else max_seq_len)
+        cbk, cbv = self.codebooks[l]
+        return abi.loopkv_vq_append(self.dims, self.pools[l], self.num_pages, cbk, cbv, batch,
+                                    int(k.shape[2]), k, v)
+
+    def prefill_layer(self, l: int, keep=None):
+        """Code every sequence's prefill tokens, one sequence per call.
+        keep: set of sequences whose bf16 (K, V) stay on the host."""
+        kept = {}
+        for b in range(self.w.batch):
+            T = int(self.lens0[b])
+            if T == 0:
+                continue
+            k, v = wl.vq_kv(self.w, l, b, 0, T, self.device)
+            self.append(l, k, v, self._zero, table=self.block_tables[b:b + 1])
+            if keep and b in keep:
+                kept[b] = (wl.bf16_bits(k[:, 0]), wl.bf16_bits(v[:, 0]))    # [R][T][H][D]
+        return kept
+
+    def decode(self, l: int, loop: int, q, out, lens=None, sm_scale: float = 1.0):
+        batch = abi.make_batch(self.lens if lens is None else lens, self.block_tables, self.max_seq_len)
+        cbk, cbv = self.codebooks[l]
+        return abi.loopkv_vq_decode(self.dims, self.pools[l], self.num_pages, cbk, cbv, loop, batch, q, out,
+                                    self.workspace, sm_scale)
+
+    def pool_indices(self, l: int, b: int, T: int):
+        """Host copy of sequence b's (key, value) indices [T][H][D/4] from the pool."""
+        import torch
+        P, H, G = self.w.page, self.w.heads, self.w.head_dim // 4
+        n = -(-T // P)
+        pages = torch.from_numpy(self.table_np[b, :n].astype(np.int64)).to(self.device)
+        blk = self.pools[l].view(H, self.num_pages, 2, P, G).index_select(1, pages).cpu().numpy()
+        k = blk[:, :, 0].reshape(H, n * P, G)[:, :T].transpose(1, 0, 2)
+        v = blk[:, :, 1].reshape(H, n * P, G)[:, :T].transpose(1, 0, 2)
+        return k, v

@@ -29,6 +29,10 @@ Modules
 codec      group quantizer, bit planes, 2-bit row packing
 cache      per-sequence cell cache and its paged byte layout
 attention  decode of one cell: scores, softmax, tau mask, output
+planner    offline plan search by exhaustive enumeration (small grids)
+loopvq     joint vector quantization across loop steps and its decode
+           ("LoopVQ: Sub 1-bit KV Cache Quantization for Looped
+           Transformers", abstract)
 
 Parity status of every function is listed in each module's header.  No
 function here is "parity unpinned": each is pinned by tests under

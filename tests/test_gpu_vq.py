@@ -1,0 +1,131 @@
+"""GPU parity of the joint loop-step vector quantization path (LoopVQ-style)
+against oracle/loopvq.py, through the C ABI.
+
+Bar: a stored index equals the oracle's nearest codeword, or (near-ties
+decided in fp32) one whose float64 distance is within 1e-5 relative of the
+least; decoded outputs within 2e-3 of the output's L_inf norm per compared
+block, the oracle decoding the GPU's (checked) indices.
+"""
+import numpy as np
+import pytest
+
+from loop_aware_quantized_amd import inputs as wl
+from loop_aware_quantized_amd import runner
+from oracle import loopvq as ov
+from parity_util import say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+OUT_TOL = 2e-3
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.empty_cache()
+
+
+def bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_indices(gpu_idx, x_loops_bits, codebook):
+    """gpu_idx [T][H][G]; x_loops_bits uint16 [R][T][H][D] -> exact-match fraction."""
+    cb = codebook.float().cpu().numpy().astype(np.float64)
+    x = bf16_to_f64(x_loops_bits)
+    exact = total = 0
+    for h in range(x.shape[2]):
+        d = ov.distances(x[:, :, h, :], cb)                    # [T][G][256]
+        dmin = d.min(-1)
+        got = np.take_along_axis(d, gpu_idx[:, h, :, None].astype(np.int64), -1)[..., 0]
+        bad = got > dmin * (1 + 1e-5) + 1e-9
+        assert not bad.any(), f"head {h}: {bad.sum()} indices are not nearest codewords"
+        exact += int((gpu_idx[:, h, :] == np.argmin(d, -1)).sum())
+        total += gpu_idx[:, h, :].size
+    return exact / max(total, 1)
+
+
+def compare(st, l, loop, q, out, kept, seqs, lens):
+    cbk, cbv = (c.float().cpu().numpy().astype(np.float64) for c in st.codebooks[l])
+    qh = bf16_to_f64(wl.bf16_bits(q))
+    oh = out.cpu().numpy()
+    errs, scale = [], 0.0
+    for b in seqs:
+        T = int(lens[b])
+        ki, vi = st.pool_indices(l, b, T)
+        for h in range(st.w.heads):
+            k_hat = ov.decode_loop(ki[:, h].astype(np.int64), cbk, loop)
+            v_hat = ov.decode_loop(vi[:, h].astype(np.int64), cbv, loop)
+            want = ov.attend(qh[b, h], k_hat, v_hat)
+            errs.append(np.abs(oh[b, h] - want).max())
+            scale = max(scale, np.abs(want).max())
+    err = max(errs)
+    assert np.all(np.isfinite(oh))
+    assert err <= OUT_TOL * max(scale, 1e-30), f"layer {l} loop {loop}: err {err:.3e} vs {scale:.3e}"
+    return err / max(scale, 1e-30)
+
+
+def test_vq_tiny_end_to_end():
+    w = wl.VQ_WORKLOADS["loopvq-tiny"]
+    lens = [300, 57]
+    st = runner.VqState(w, DEV, lengths=lens)
+    for l in st.layers:
+        kept = st.prefill_layer(l, keep={0, 1})
+        torch.cuda.synchronize()
+        for b in (0, 1):
+            ki, vi = st.pool_indices(l, b, lens[b])
+            fk = check_indices(ki, kept[b][0], st.codebooks[l][0])
+            fv = check_indices(vi, kept[b][1], st.codebooks[l][1])
+            say(f"  layer {l} seq {b}: exact index matches K {fk:.4f} V {fv:.4f}")
+        for loop in range(w.loops):
+            q = wl.vq_query(w, l, loop, DEV)
+            out = torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=DEV)
+            st.decode(l, loop, q, out)
+            torch.cuda.synchronize()
+            rel = compare(st, l, loop, q, out, kept, (0, 1), lens)
+            say(f"  layer {l} loop {loop}: rel err {rel:.2e}")
+
+
+def test_vq_empty_sequence_and_appends():
+    w = wl.VqWorkload("vq-append", 12, batch=3, loops=2, layers=1, heads=2, head_dim=128, page=32, ctx=100)
+    lens = np.array([100, 0, 33], np.int32)
+    st = runner.VqState(w, DEV, lengths=lens, extra_tokens=5)
+    st.prefill_layer(0)
+    # five single-token appends to every sequence
+    for step in range(5):
+        k, v = wl.vq_append_kv(w, 0, step, 1, DEV)
+        st.append(0, k, v, torch.from_numpy(lens + step).to(DEV))
+    lens_now = lens + 5
+    torch.cuda.synchronize()
+    q = wl.vq_query(w, 0, 1, DEV)
+    out = torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=DEV)
+    st.decode(0, 1, q, out, lens=torch.from_numpy(lens_now).to(DEV))
+    torch.cuda.synchronize()
+    compare(st, 0, 1, q, out, None, (0, 1, 2), lens_now)
+    # a zero-length batch entry decodes to zeros
+    zero = torch.from_numpy(np.array([0, 0, 0], np.int32)).to(DEV)
+    st.decode(0, 0, q, out, lens=zero)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out) == 0
+
+
+def test_vq_16k_sampled():
+    w = wl.VQ_WORKLOADS["loopvq-16k"]
+    seqs = [0, 31]
+    st = runner.VqState(w, DEV, layers=[5])
+    kept = st.prefill_layer(5, keep=set(seqs))
+    torch.cuda.synchronize()
+    for b in seqs:
+        ki, _ = st.pool_indices(5, b, w.ctx)
+        f = check_indices(ki[:2048], kept[b][0][:, :2048], st.codebooks[5][0])
+        say(f"  seq {b}: exact key index matches (first 2048 tokens) {f:.5f}")
+    for loop in range(w.loops):
+        q = wl.vq_query(w, 5, loop, DEV)
+        out = torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=DEV)
+        st.decode(5, loop, q, out)
+        torch.cuda.synchronize()
+        rel = compare(st, 5, loop, q, out, kept, seqs, st.lens0)
+        say(f"  loop {loop}: rel err {rel:.2e}")
