@@ -369,6 +369,95 @@ def cpu_baseline(w, st, kinds, taus, n_samples, dev):
             "seconds": t_total}
 
 
+def vq_main(args, w):
+    """Bench of a LoopVQ-style workload: per step, every layer codes one
+    appended token (all loops jointly) and every (loop, layer) cell decodes."""
+    import torch
+    from loop_aware_quantized_amd import abi, runner
+    from loop_aware_quantized_amd import inputs as wl
+    dev = torch.device("cuda", 0)
+    steps_total = args.warmup + args.steps + 1
+    t0 = time.time()
+    st = runner.VqState(w, dev, extra_tokens=w.append_tokens * steps_total)
+    for l in st.layers:
+        st.prefill_layer(l)
+        if l % 8 == 7:
+            torch.cuda.synchronize()
+            log(f"[bench] {w.name}: prefilled {l + 1}/{w.layers} layers ({time.time() - t0:.1f} s)")
+    torch.cuda.synchronize()
+    R, L, B, H, D = w.loops, w.layers, w.batch, w.heads, w.head_dim
+    queries = {(r, l): wl.vq_query(w, l, r, dev) for r in range(R) for l in range(L)}
+    new_kv = {l: wl.vq_append_kv(w, l, 0, w.append_tokens, dev) for l in range(L)} if w.append_tokens else {}
+    lens0 = st.lens0.astype(np.int64)
+    lens_dev = [torch.from_numpy((lens0 + s * w.append_tokens).astype(np.int32)).to(dev)
+                for s in range(steps_total + 1)]
+    out = torch.empty(B, H, D, dtype=torch.float32, device=dev)
+    state = {"s": 0}
+
+    def lens_of(s):
+        return lens0 + (s + 1) * w.append_tokens
+
+    def step():
+        s = state["s"]
+        if w.append_tokens:
+            for l in range(L):
+                st.append(l, *new_kv[l], lens_dev[s])
+        ld = lens_dev[s + 1] if w.append_tokens else lens_dev[0]
+        for r in range(R):
+            for l in range(L):
+                st.decode(l, r, queries[(r, l)], out, lens=ld)
+        state["s"] += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    first = state["s"]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    abi.loopkv_profile_enable(True)
+    for c in (abi.KERNEL_SPLIT, abi.KERNEL_MERGE, abi.KERNEL_APPEND):
+        abi.loopkv_profile_collect(c)
+    prof = state["s"]
+    step()
+    torch.cuda.synchronize()
+    kst = {n: abi.loopkv_profile_collect(c) for n, c in
+           (("split", abi.KERNEL_SPLIT), ("merge", abi.KERNEL_MERGE), ("append", abi.KERNEL_APPEND))}
+    abi.loopkv_profile_enable(False)
+    tokens = sum(int(lens_of(s).sum()) for s in range(first, first + args.steps)) / args.steps
+    per_th = 2 * (D // 4)                           # key + value index bytes per token-head
+    step_bytes = R * L * (tokens * H * per_th + B * H * 6 * D)
+    split_bytes = R * L * int(lens_of(prof).sum()) * H * per_th
+    n_split, split_ms = kst["split"]
+    achieved = split_bytes / (split_ms / 1e3) / 1e9
+    stored = L * abi.vq_pool_bytes(st.dims, st.num_pages)
+    res = {
+        "metric": METRIC, "value": tokens * R * L / (ms / 1e3), "unit": "KV tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded loop-redundant bf16 K/V, synthetic codebooks)",
+        "config": {"workload": w.name, "batch": B, "loops": R, "layers": L, "heads": H, "head_dim": D,
+                   "page": w.page, "context": int(lens_of(first).max()), "bits_per_element": 8 / (4 * R),
+                   "append_tokens_per_step": w.append_tokens},
+        "hbm_gbs_required": step_bytes / (ms / 1e3) / 1e9,
+        "roofline": {"bound": "hbm", "kernel": "vq_split_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "launches": n_split, "avg_launch_us": split_ms * 1e3 / max(n_split, 1)},
+        "kernels_ms_per_step": {k: v[1] for k, v in kst.items()},
+        "storage": {"stored_bytes": stored},
+        "cpu_baseline": None,
+    }
+    line = json.dumps(res)
+    if args.report:
+        with open(args.report, "w") as f:
+            f.write(line + "\n")
+    print(line, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -393,6 +482,9 @@ def main():
     torch.cuda.set_device(0)
     abi.lib()  # fail loudly if the HIP library is missing
 
+    if args.workload in wl.VQ_WORKLOADS:
+        vq_main(args, wl.VQ_WORKLOADS[args.workload])
+        return
     w = wl.WORKLOADS[args.workload]
     kinds, taus = wl.make_plan(w)
     if args.tau is not None:

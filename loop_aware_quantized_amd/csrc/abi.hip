@@ -493,12 +493,14 @@ struct VqSplits {
   int S, len;
 };
 
-// Splits of 2048 tokens when that still gives four blocks per compute unit
-// (two are resident at a time), else of 1024.
+// One block of 8 waves per compute unit is resident (its tables fill most
+// of the LDS): splits as long as possible (up to kVqSplitMax tokens, whole
+// chunks) while giving at least two blocks per compute unit.
 VqSplits vq_splits(int64_t batch, int64_t heads, int t_max) {
   const int64_t tm = std::max<int64_t>(t_max, 1);
-  int64_t len = lkv::kVqSplitMax;
-  if (batch * heads * ((tm + len - 1) / len) < static_cast<int64_t>(cu_count()) * 4) len = lkv::kVqSplitMax / 2;
+  int64_t s0 = std::max<int64_t>(1, (2 * static_cast<int64_t>(cu_count()) + batch * heads - 1) / (batch * heads));
+  s0 = std::max<int64_t>(s0, (tm + lkv::kVqSplitMax - 1) / lkv::kVqSplitMax);
+  const int64_t len = std::min<int64_t>(round_up((tm + s0 - 1) / s0, lkv::kVqChunk), lkv::kVqSplitMax);
   return {static_cast<int>((tm + len - 1) / len), static_cast<int>(len)};
 }
 
@@ -516,7 +518,7 @@ size_t loopkv_vq_pool_bytes(const loopkv_vq_dims* d, int64_t num_pages) {
 
 size_t loopkv_vq_workspace_bytes(const loopkv_vq_dims* d, int32_t batch, int32_t max_seq_len) {
   if (vq_dims_error(d) || batch < 0 || max_seq_len < 0) return 0;
-  const int64_t s_max = (std::max<int64_t>(max_seq_len, 1) + lkv::kVqSplitMax / 2 - 1) / (lkv::kVqSplitMax / 2);
+  const int64_t s_max = (std::max<int64_t>(max_seq_len, 1) + lkv::kVqChunk - 1) / lkv::kVqChunk;
   return static_cast<size_t>(round_up(static_cast<int64_t>(batch) * d->heads * s_max * (d->head_dim + lkv::kPartialPad) * 4, 256));
 }
 

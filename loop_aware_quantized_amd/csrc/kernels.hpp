@@ -69,10 +69,11 @@ hipError_t launch_merge_plain(const DecodeArgs& a, int batch, hipStream_t stream
 // ---- joint vector quantization across loop steps (LoopVQ-style) ---------
 constexpr int kVqSub = 4;            // channels per loop in one joint vector
 constexpr int kVqCodes = 256;        // codewords per codebook (8-bit index)
-constexpr int kVqSplitMax = 2048;    // tokens per decode split (LDS scores)
+constexpr int kVqChunk = 1024;      // tokens per score pass of a decode split (LDS scores)
+constexpr int kVqSplitMax = 8192;    // tokens per decode split
 
 struct VqArgs {
-  uint8_t* pool;                     // [H][num_pages][2][P][D/4] indices (K rows, V rows)
+  uint8_t* pool;                     // [H][num_pages]: [P][D/4] key, [4][P][D/16] value indices
   const uint16_t* cb_k;              // [D/4][256][4R] fp16 codebook of the keys
   const uint16_t* cb_v;              // same for the values
   const int32_t* seq_lens;
