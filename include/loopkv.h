@@ -291,9 +291,9 @@ int loopkv_vq_append(const loopkv_vq_dims* dims, void* pool, int64_t num_pages,
  * cache: keys and values are the loop's slices (positions 4*loop ..
  * 4*loop+3) of the chosen codewords; o = softmax(sm_scale * q.K^) V^.
  * q_bf16: device [B][H][D] bfloat16 (8-byte aligned); out: device fp32
- * [B][H][D].  A sequence of length 0 produces zeros.  Value weights are
- * accumulated with float atomics, so the last bits of out may differ
- * between runs.
+ * [B][H][D].  A sequence of length 0 produces zeros.  The summation
+ * order is fixed by the launch shape, so repeated calls with the same
+ * inputs and workspace size give identical bits.
  * Errors: LOOPKV_E_INVAL, LOOPKV_E_CAPACITY (workspace too small),
  *   LOOPKV_E_HIP.
  */

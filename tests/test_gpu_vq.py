@@ -87,6 +87,10 @@ def test_vq_tiny_end_to_end():
             torch.cuda.synchronize()
             rel = compare(st, l, loop, q, out, kept, (0, 1), lens)
             say(f"  layer {l} loop {loop}: rel err {rel:.2e}")
+            again = torch.empty_like(out)
+            st.decode(l, loop, q, again)
+            torch.cuda.synchronize()
+            assert torch.equal(out, again), "fixed summation order: repeated calls give identical bits"
 
 
 def test_vq_empty_sequence_and_appends():
