@@ -253,9 +253,8 @@ int loopkv_plan_optimize(int32_t R, int32_t L, const double* damage, double dama
  * Codebook (one layer, keys or values): device fp16 [D/4][256][4R].
  * Pool: device, head-major like the cell pools: head h of physical page p
  *   at byte (h*num_pages + p) * 2*P*(D/4); inside, P key index rows of D/4
- *   bytes (token-major), then the value indices chunk-major: 4 chunks of
- *   D/16 groups, [4][P][D/16] bytes (group j of token t at
- *   ((j / (D/16)) * P + t) * (D/16) + j % (D/16)).
+ *   bytes (token-major), then P value index rows of D/4 bytes (group j of
+ *   token t: key at t*(D/4) + j, value at (P + t)*(D/4) + j).
  */
 typedef struct {
   int32_t loops;       /* R, 2..4 */

@@ -494,13 +494,14 @@ struct VqSplits {
 };
 
 // One block of 8 waves per compute unit is resident (its tables fill most
-// of the LDS): splits as long as possible (up to kVqSplitMax tokens, whole
-// chunks) while giving at least two blocks per compute unit.
+// of the LDS) and every block first builds its tables: as few splits as
+// fill the compute units once, each a whole number of 512-token units and
+// at most kVqSplitMax tokens.
 VqSplits vq_splits(int64_t batch, int64_t heads, int t_max) {
   const int64_t tm = std::max<int64_t>(t_max, 1);
-  int64_t s0 = std::max<int64_t>(1, (2 * static_cast<int64_t>(cu_count()) + batch * heads - 1) / (batch * heads));
+  int64_t s0 = std::max<int64_t>(1, (static_cast<int64_t>(cu_count()) + batch * heads - 1) / (batch * heads));
   s0 = std::max<int64_t>(s0, (tm + lkv::kVqSplitMax - 1) / lkv::kVqSplitMax);
-  const int64_t len = std::min<int64_t>(round_up((tm + s0 - 1) / s0, lkv::kVqChunk), lkv::kVqSplitMax);
+  const int64_t len = std::min<int64_t>(round_up((tm + s0 - 1) / s0, lkv::kVqSplitUnit), lkv::kVqSplitMax);
   return {static_cast<int>((tm + len - 1) / len), static_cast<int>(len)};
 }
 
@@ -518,7 +519,7 @@ size_t loopkv_vq_pool_bytes(const loopkv_vq_dims* d, int64_t num_pages) {
 
 size_t loopkv_vq_workspace_bytes(const loopkv_vq_dims* d, int32_t batch, int32_t max_seq_len) {
   if (vq_dims_error(d) || batch < 0 || max_seq_len < 0) return 0;
-  const int64_t s_max = (std::max<int64_t>(max_seq_len, 1) + lkv::kVqChunk - 1) / lkv::kVqChunk;
+  const int64_t s_max = (std::max<int64_t>(max_seq_len, 1) + lkv::kVqSplitUnit - 1) / lkv::kVqSplitUnit;
   return static_cast<size_t>(round_up(static_cast<int64_t>(batch) * d->heads * s_max * (d->head_dim + lkv::kPartialPad) * 4, 256));
 }
 
@@ -606,8 +607,13 @@ int loopkv_vq_decode(const loopkv_vq_dims* d, const void* pool, int64_t num_page
   a.S = sp.S;
   a.split_len = sp.len;
   a.sm_scale = sm_scale;
+  a.out = out;
   hipError_t e = lkv::launch_vq_split(a, d->head_dim, s);
   if (e != hipSuccess) return fail_hip(e, "vq_decode: split kernel launch");
+  if (sp.S == 1) {         // the split pass wrote the output
+    g_err.clear();
+    return LOOPKV_OK;
+  }
   lkv::DecodeArgs m{};
   m.seq_lens = batch->seq_lens;
   m.block_tables = batch->block_tables;

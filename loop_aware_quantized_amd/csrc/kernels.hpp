@@ -69,11 +69,11 @@ hipError_t launch_merge_plain(const DecodeArgs& a, int batch, hipStream_t stream
 // ---- joint vector quantization across loop steps (LoopVQ-style) ---------
 constexpr int kVqSub = 4;            // channels per loop in one joint vector
 constexpr int kVqCodes = 256;        // codewords per codebook (8-bit index)
-constexpr int kVqChunk = 1024;      // tokens per score pass of a decode split (LDS scores)
-constexpr int kVqSplitMax = 8192;    // tokens per decode split
+constexpr int kVqSplitUnit = 512;   // decode split lengths are multiples of this (8 waves x 64 tokens)
+constexpr int kVqSplitMax = 32768;   // tokens per decode split
 
 struct VqArgs {
-  uint8_t* pool;                     // [H][num_pages]: [P][D/4] key, [4][P][D/16] value indices
+  uint8_t* pool;                     // [H][num_pages]: [P][D/4] key, then [P][D/4] value indices
   const uint16_t* cb_k;              // [D/4][256][4R] fp16 codebook of the keys
   const uint16_t* cb_v;              // same for the values
   const int32_t* seq_lens;
@@ -82,6 +82,7 @@ struct VqArgs {
   const uint16_t* v_in;
   const uint16_t* q;                 // decode: [B][H][D] bf16
   float* partials;                   // decode: [B][H][S][D + kPartialPad]
+  float* out;                        // decode: [B][H][D], written by the split pass when S == 1
   int64_t num_pages;
   int32_t R, batch, H, P, max_pages, n_new, loop, S, split_len;
   float sm_scale;

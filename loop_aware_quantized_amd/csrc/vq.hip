@@ -14,21 +14,21 @@
 // codeword.
 //
 // Layout of a head-block (one head, one page of P tokens): P key index
-// rows of D/4 bytes (token-major), then the value indices in four chunks of
-// D/16 groups each, chunk-major: [4][P][D/16] bytes, so the wave that owns a
-// chunk reads its bytes of 64 tokens as one contiguous run.
+// rows of D/4 bytes, then P value index rows of D/4 bytes (token-major), so
+// the 64 lanes of a wave read one 64-token tile's rows as contiguous runs.
 //
-// Decode of loop r, one 512-thread block (8 waves) per (split, head,
-// sequence), a split streamed in chunks of 1024 tokens:
+// Decode of loop r, one block of 8 waves per (split, head, sequence):
 //   1. a table lut[j][c] = sm_scale * q[4j..4j+4) . key codeword_c[4r..4r+4)
 //      and the loop's value codeword slices, both in LDS, so a token's score
 //      is the sum of D/4 table reads addressed by its key bytes;
-//   2. the chunk's scores and maximum (running max across chunks);
-//   3. wave w owns value chunk w % 4 and every other 64-token tile: per
-//      token p_t = exp(s_t - max) and, per group of the chunk, one LDS read
-//      of the 4 fp16 channels of the chosen codeword and 4 FMAs;
-//   4. lanes, then the two waves of a chunk, are summed: (max, sum, o).
-// The partials are merged by the plain log-sum-exp merge.
+//   2. each wave streams its own 64-token tiles (lane = token) with a
+//      private online softmax: score, wave maximum (accumulators rescaled
+//      only when it rises), p_t, and per value group one LDS read of the 4
+//      fp16 channels of the chosen codeword and 4 FMAs into the lane's D
+//      accumulators;
+//   3. lanes are summed by a butterfly, waves through LDS: (max, sum, o).
+// With several splits the partials are merged by the plain log-sum-exp
+// merge; with one the block writes o / sum.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -36,7 +36,8 @@ namespace lkv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokPerThread = 4;     // tokens per thread per step (loads in flight)
+constexpr int kSplitWaves = 8;
+constexpr int kSplitThreads = 64 * kSplitWaves;
 
 // Encode: one thread per (sequence, new token, head), a block per 256 of
 // them and per channel group (blockIdx.y); blockIdx.z = 0 keys, 1 values.
@@ -88,33 +89,35 @@ __global__ __launch_bounds__(kThreads) void vq_encode_kernel(VqArgs a) {
   const int32_t page = a.block_tables[static_cast<int64_t>(b) * a.max_pages + t / a.P];
   const int64_t hb = static_cast<int64_t>(2) * a.P * G;
   uint8_t* blk = a.pool + (static_cast<int64_t>(h) * a.num_pages + page) * hb;
-  if (is_v) {
-    constexpr int kCg = G / 4;     // groups per value chunk
-    blk[a.P * G + ((j / kCg) * a.P + t % a.P) * kCg + j % kCg] = static_cast<uint8_t>(best_c);
-  } else {
-    blk[(t % a.P) * G + j] = static_cast<uint8_t>(best_c);
-  }
+  blk[(is_v ? a.P * G : 0) + (t % a.P) * G + j] = static_cast<uint8_t>(best_c);
 }
 
-// Split pass of the decode of loop a.loop: a block streams its split in
-// chunks of kVqChunk tokens with an online softmax (running max and sum;
-// accumulators rescaled when the max rises).  The key rows of the next chunk
-// and the value bytes of the next tile are loaded before the current ones
-// are used.
-constexpr int kSplitThreads = 512;
+// Split pass of the decode of loop a.loop: one block of kSplitWaves waves
+// per (split, head, sequence).  After the block has built its two tables,
+// every wave streams its own 64-token tiles (tiles w, w + kSplitWaves, ...
+// of the split) with a private online softmax and no barrier: lane = token;
+// the key row gives the score by D/4 table reads; a running wave maximum
+// rescales the lane's D accumulators only when it rises; the value row adds
+// p * (codeword slice) group by group.  The next tile's rows are loaded
+// while the current one is used.  At the end the lanes of a wave are summed
+// by a butterfly (each lane keeps D/64 channels) and the waves are combined
+// through LDS with their maxima.  With one split the block writes the
+// normalized output itself.
 template <int D, int R>
 __global__ __launch_bounds__(kSplitThreads) void vq_split_kernel(VqArgs a) {
-  constexpr int G = D / kVqSub;      // index bytes per key row
+  constexpr int G = D / kVqSub;      // index bytes per row
   constexpr int J = kVqSub * R;
-  constexpr int kWords = G / 16;     // 16-byte words per key row
-  constexpr int kCg = G / 4;         // groups per value chunk
-  constexpr int kAcc = kVqSub * kCg; // channels per value chunk
-  constexpr int kTok = kVqChunk / kSplitThreads;   // tokens per thread per score pass
-  __shared__ float lut[G * kVqCodes];
-  __shared__ uint2 cvs[G * kVqCodes];     // value codeword slices of the loop (4 x fp16)
-  __shared__ float sc[kVqChunk];
-  __shared__ float red[kSplitThreads / 64];
-  __shared__ float ored[4 * kAcc];
+  constexpr int kWords = G / 16;     // 16-byte words per index row
+  constexpr int kKeep = D / 64;      // channels a lane holds after the butterfly
+  // one LDS block, score table first: its row offsets (and those of the
+  // first 64 KB of codeword slices) fit the LDS instructions' 16-bit offset
+  constexpr int kLut = G * kVqCodes * 4, kCvs = G * kVqCodes * 8, kOut = kSplitWaves * D * 4;
+  __shared__ __align__(16) unsigned char smem[kLut + kCvs + kOut + 2 * kSplitWaves * 4];
+  float* lut = reinterpret_cast<float*>(smem);
+  uint2* cvs = reinterpret_cast<uint2*>(smem + kLut);      // value codeword slices of the loop (4 x fp16)
+  float* wout = reinterpret_cast<float*>(smem + kLut + kCvs);
+  float* wmax = wout + kSplitWaves * D;
+  float* wsum = wmax + kSplitWaves;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -122,42 +125,45 @@ __global__ __launch_bounds__(kSplitThreads) void vq_split_kernel(VqArgs a) {
   const int T = a.seq_lens[b];
   const int start = split * a.split_len;
   const int end = min(start + a.split_len, T);
-  if (start >= end) return;
   const int64_t pair = static_cast<int64_t>(b) * a.H + h;
+  if (start >= end) {
+    if (a.S == 1 && tid < D) a.out[pair * D + tid] = 0.0f;     // empty sequence
+    return;
+  }
 
   const int lgP = __builtin_ctz(static_cast<unsigned>(a.P));
   const int pmask = a.P - 1;
   const int64_t hb = static_cast<int64_t>(2) * a.P * G;
   const uint8_t* head = a.pool + static_cast<int64_t>(h) * a.num_pages * hb;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_pages;
+  const int n_tiles = (end - start + 63) >> 6;
 
-  // key rows of one chunk, kTok per thread
-  auto load_keys = [&](uint4 (&w)[kTok][kWords], int c0) {
+  // key and value index rows of this lane's token in one tile; a lane past
+  // the end (or a tile past the split) reads the split's last token, whose
+  // score is then masked
+  auto load_rows = [&](uint4 (&kr)[kWords], uint4 (&vr)[kWords], int tile) {
+    const int t = min(start + 64 * tile + lane, end - 1);
+    const uint8_t* row = head + static_cast<int64_t>(bt[t >> lgP]) * hb + (t & pmask) * G;
 #pragma unroll
-    for (int u = 0; u < kTok; ++u) {
-      const int t = c0 + u * kSplitThreads + tid;
-#pragma unroll
-      for (int k = 0; k < kWords; ++k) {
-        w[u][k] = make_uint4(0u, 0u, 0u, 0u);
-        if (t < end)
-          w[u][k] = reinterpret_cast<const uint4*>(head + static_cast<int64_t>(bt[t >> lgP]) * hb + (t & pmask) * G)[k];
-      }
+    for (int k = 0; k < kWords; ++k) {
+      kr[k] = reinterpret_cast<const uint4*>(row)[k];
+      vr[k] = reinterpret_cast<const uint4*>(row + a.P * G)[k];
     }
   };
-  uint4 kw[kTok][kWords];
-  load_keys(kw, start);
+  uint4 kr[kWords], vr[kWords];
+  load_rows(kr, vr, wave);
 
-  // 1. score table and value codeword slices (thread = codeword; all loads of
-  //    a batch of groups issued before use)
+  // score table and value codeword slices (thread = codeword; all loads of a
+  // batch of groups issued before use)
   {
     const int c = tid & (kVqCodes - 1);
-    constexpr int kStep = kSplitThreads / kVqCodes;     // 2
+    constexpr int kStep = kSplitThreads / kVqCodes;
     constexpr int kBatch = 4;
-    for (int j0 = tid >> 8; j0 < G; j0 += kStep * kBatch) {
+    for (int j0 = tid / kVqCodes; j0 < G; j0 += kStep * kBatch) {
       uint2 qw[kBatch], kc[kBatch], vc[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        const int j = j0 + kStep * u;
+        const int j = min(j0 + kStep * u, G - 1);
         const int64_t cwo = (static_cast<int64_t>(j) * kVqCodes + c) * J + kVqSub * a.loop;
         qw[u] = *reinterpret_cast<const uint2*>(a.q + pair * D + kVqSub * j);
         kc[u] = *reinterpret_cast<const uint2*>(a.cb_k + cwo);
@@ -166,6 +172,7 @@ __global__ __launch_bounds__(kSplitThreads) void vq_split_kernel(VqArgs a) {
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int j = j0 + kStep * u;
+        if (j >= G) break;
         float s = bf16_to_f32(static_cast<uint16_t>(qw[u].x & 0xffffu)) * f16_to_f32(kc[u].x & 0xffffu);
         s = fmaf(bf16_to_f32(static_cast<uint16_t>(qw[u].x >> 16)), f16_to_f32(kc[u].x >> 16), s);
         s = fmaf(bf16_to_f32(static_cast<uint16_t>(qw[u].y & 0xffffu)), f16_to_f32(kc[u].y & 0xffffu), s);
@@ -177,113 +184,109 @@ __global__ __launch_bounds__(kSplitThreads) void vq_split_kernel(VqArgs a) {
   }
   __syncthreads();
 
-  const int chunk = wave & 3, half = wave >> 2;   // value chunk and tile parity of this wave
-  constexpr int kTiles = kVqChunk / 128;          // value tiles of a wave per chunk
-  // value bytes of this wave's tiles of one chunk (lane = token slot)
-  auto load_vals = [&](uint2 (&v)[kTiles], int c0) {
-    const int c1 = min(c0 + kVqChunk, end);
+  float acc[D];
 #pragma unroll
-    for (int i = 0; i < kTiles; ++i) {
-      const int t = c0 + 64 * half + 128 * i + lane;
-      v[i] = make_uint2(0u, 0u);
-      if (t < c1) {
-        const uint8_t* vb = head + static_cast<int64_t>(bt[t >> lgP]) * hb + a.P * G + (chunk * a.P + (t & pmask)) * kCg;
-        if (kCg == 8) v[i] = *reinterpret_cast<const uint2*>(vb);
-        else v[i].x = *reinterpret_cast<const uint32_t*>(vb);
-      }
-    }
-  };
-  uint2 vw[kTiles];
-  load_vals(vw, start);
-  float acc[kAcc];
-#pragma unroll
-  for (int i = 0; i < kAcc; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < D; ++i) acc[i] = 0.0f;
   float M = -INFINITY, lsum = 0.0f;
 
-  for (int c0 = start; c0 < end; c0 += kVqChunk) {
-    const int c1 = min(c0 + kVqChunk, end);
-    // 2. scores of the chunk and its maximum
-    float mloc = -INFINITY;
+  for (int tile = wave; tile < n_tiles; tile += kSplitWaves) {
+    uint4 kn[kWords], vn[kWords];
+    load_rows(kn, vn, tile + kSplitWaves);
+    const int t = start + 64 * tile + lane;
+    // score: D/4 table reads, four partial sums
+    float sp[4];
 #pragma unroll
-    for (int u = 0; u < kTok; ++u) {
-      const int t = c0 + u * kSplitThreads + tid;
-      float s = 0.0f;
+    for (int k = 0; k < kWords; ++k) {
+      const uint32_t ws[4] = {kr[k].x, kr[k].y, kr[k].z, kr[k].w};
 #pragma unroll
-      for (int k = 0; k < kWords; ++k) {
-        const uint32_t ws[4] = {kw[u][k].x, kw[u][k].y, kw[u][k].z, kw[u][k].w};
-#pragma unroll
-        for (int q = 0; q < 16; ++q) s += lut[(16 * k + q) * kVqCodes + ((ws[q / 4] >> (8 * (q % 4))) & 0xffu)];
-      }
-      if (t < c1) {
-        sc[t - c0] = s;
-        mloc = fmaxf(mloc, s);
-      }
-    }
-    // the next chunk's key rows and value bytes are in flight from here on
-    uint2 vn[kTiles];
-    if (c0 + kVqChunk < end) {
-      load_keys(kw, c0 + kVqChunk);
-      load_vals(vn, c0 + kVqChunk);
-    }
-    mloc = wave_max(mloc);
-    if (lane == 0) red[wave] = mloc;
-    __syncthreads();
-    float mc = red[0];
-#pragma unroll
-    for (int i = 1; i < kSplitThreads / 64; ++i) mc = fmaxf(mc, red[i]);
-    const float m_new = fmaxf(M, mc);
-    const float alpha = __expf(M - m_new);                    // 0 on the first chunk
-#pragma unroll
-    for (int i = 0; i < kAcc; ++i) acc[i] *= alpha;
-    lsum *= alpha;
-    M = m_new;
-
-    // 3. values: wave w owns chunk w % 4 and every other 64-token tile
-#pragma unroll
-    for (int i = 0; i < kTiles; ++i) {
-      const int t = c0 + 64 * half + 128 * i + lane;
-      if (t < c1) {
-        const float p = __expf(sc[t - c0] - M);
-        lsum += p;
-        const uint32_t bytes[2] = {vw[i].x, vw[i].y};
-#pragma unroll
-        for (int g = 0; g < kCg; ++g) {
-          const int code = (bytes[g / 4] >> (8 * (g % 4))) & 0xff;
-          const uint2 cw = cvs[(kCg * chunk + g) * kVqCodes + code];
-          acc[4 * g + 0] = fmaf(p, f16_to_f32(cw.x & 0xffffu), acc[4 * g + 0]);
-          acc[4 * g + 1] = fmaf(p, f16_to_f32(cw.x >> 16), acc[4 * g + 1]);
-          acc[4 * g + 2] = fmaf(p, f16_to_f32(cw.y & 0xffffu), acc[4 * g + 2]);
-          acc[4 * g + 3] = fmaf(p, f16_to_f32(cw.y >> 16), acc[4 * g + 3]);
-        }
+      for (int q = 0; q < 16; ++q) {
+        // byte offset of the entry in its row; kept opaque so that the row's
+        // offset goes into the LDS instruction's immediate field
+        uint32_t off = ((ws[q / 4] >> (8 * (q % 4))) & 0xffu) << 2;
+        asm volatile("" : "+v"(off));
+        const float e = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut + (16 * k + q) * kVqCodes) + off);
+        if (k == 0 && q < 4) sp[q] = e;
+        else sp[q % 4] += e;
       }
     }
-    if (c0 + kVqChunk < end) {
+    const float s = t < end ? (sp[0] + sp[1]) + (sp[2] + sp[3]) : -INFINITY;
+    const float mt = dpp_wave_max(s);      // wave-uniform; finite (lane 0 is in range)
+    if (mt > M) {
+      const float alpha = __expf(M - mt);  // 0 on the first tile
 #pragma unroll
-      for (int i = 0; i < kTiles; ++i) vw[i] = vn[i];
+      for (int i = 0; i < D; ++i) acc[i] *= alpha;
+      lsum *= alpha;
+      M = mt;
     }
-    __syncthreads();     // sc and red are rewritten by the next chunk
+    const float p = __expf(s - M);         // 0 past the end
+    lsum += p;
+#pragma unroll
+    for (int k = 0; k < kWords; ++k) {
+      const uint32_t ws[4] = {vr[k].x, vr[k].y, vr[k].z, vr[k].w};
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int g = 16 * k + q;
+        const uint2 cw = cvs[g * kVqCodes + ((ws[q / 4] >> (8 * (q % 4))) & 0xffu)];
+        acc[4 * g + 0] = fmaf(p, f16_to_f32(cw.x & 0xffffu), acc[4 * g + 0]);
+        acc[4 * g + 1] = fmaf(p, f16_to_f32(cw.x >> 16), acc[4 * g + 1]);
+        acc[4 * g + 2] = fmaf(p, f16_to_f32(cw.y & 0xffffu), acc[4 * g + 2]);
+        acc[4 * g + 3] = fmaf(p, f16_to_f32(cw.y >> 16), acc[4 * g + 3]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kWords; ++k) {
+      kr[k] = kn[k];
+      vr[k] = vn[k];
+    }
   }
 
-  // 4. sums over lanes, then over the two waves of a chunk
+  // butterfly over the lanes: at the step of lane bit m, a lane keeps the
+  // upper half of its channels if its bit m is set, else the lower half, and
+  // adds its partner's copy of that half.
 #pragma unroll
-  for (int i = 0; i < kAcc; ++i) acc[i] = wave_sum(acc[i]);
+  for (int m = 32, n = D; m > 0; m >>= 1, n >>= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const float send = upper ? acc[i] : acc[i + n / 2];
+      const float keep = upper ? acc[i + n / 2] : acc[i];
+      acc[i] = keep + __shfl_xor(send, m, 64);
+    }
+  }
   lsum = wave_sum(lsum);
-  if (half == 1) {
+  // channel of acc[i] after the butterfly: i + sum over lane bits m of (bit set) * D / (128 / m)
+  int base = 0;
 #pragma unroll
-    for (int i = 0; i < kAcc; ++i)
-      if (lane == i) ored[chunk * kAcc + i] = acc[i];
+  for (int m = 32, n = D / 2; m > 0; m >>= 1, n >>= 1)
+    if (lane & m) base += n;
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i) wout[wave * D + base + i] = acc[i];
+  if (lane == 0) {
+    wmax[wave] = M;
+    wsum[wave] = lsum;
   }
-  if (lane == 0 && chunk == 0) red[half] = lsum;
   __syncthreads();
-  float* part = a.partials + (pair * a.S + split) * (D + kPartialPad);
-  if (half == 0) {
+  if (tid < D) {
+    float mb = wmax[0];
 #pragma unroll
-    for (int i = 0; i < kAcc; ++i)
-      if (lane == i) part[kPartialPad + kAcc * chunk + i] = acc[i] + ored[chunk * kAcc + i];
-  }
-  if (tid == 0) {
-    part[0] = M;
-    part[1] = red[0] + red[1];
+    for (int w = 1; w < kSplitWaves; ++w) mb = fmaxf(mb, wmax[w]);
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) {
+      const float f = __expf(wmax[w] - mb);   // 0 for a wave without tiles
+      o = fmaf(f, wout[w * D + tid], o);
+      l = fmaf(f, wsum[w], l);
+    }
+    if (a.S == 1) {
+      a.out[pair * D + tid] = o / l;
+    } else {
+      float* part = a.partials + (pair * a.S + split) * (D + kPartialPad);
+      part[kPartialPad + tid] = o;
+      if (tid == 0) {
+        part[0] = mb;
+        part[1] = l;
+      }
+    }
   }
 }
 

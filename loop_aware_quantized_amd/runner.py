@@ -197,6 +197,5 @@ class VqState:
         pages = torch.from_numpy(self.table_np[b, :n].astype(np.int64)).to(self.device)
         blk = self.pools[l].view(H, self.num_pages, 2 * P * G).index_select(1, pages).cpu().numpy()
         k = blk[:, :, :P * G].reshape(H, n * P, G)[:, :T].transpose(1, 0, 2)
-        # values: [4 chunks][P][G/4] per page -> [page][P][4][G/4]
-        v = blk[:, :, P * G:].reshape(H, n, 4, P, G // 4).transpose(0, 1, 3, 2, 4).reshape(H, n * P, G)
-        return k, v[:, :T].transpose(1, 0, 2)
+        v = blk[:, :, P * G:].reshape(H, n * P, G)[:, :T].transpose(1, 0, 2)
+        return k, v

@@ -133,3 +133,25 @@ def test_vq_16k_sampled():
         torch.cuda.synchronize()
         rel = compare(st, 5, loop, q, out, kept, seqs, st.lens0)
         say(f"  loop {loop}: rel err {rel:.2e}")
+
+
+@pytest.mark.parametrize("loops", [2, 3])
+def test_vq_several_splits(loops):
+    """Few sequence-heads, so every sequence is cut into several splits
+    (merged by the log-sum-exp merge), with a ragged last split."""
+    w = wl.VqWorkload(f"vq-splits-{loops}", 13, batch=2, loops=loops, layers=1, heads=2, head_dim=128,
+                      page=32, ctx=3000)
+    lens = np.array([3000, 1100], np.int32)
+    st = runner.VqState(w, DEV, lengths=lens)
+    kept = st.prefill_layer(0, keep={0, 1})
+    torch.cuda.synchronize()
+    for b in (0, 1):
+        ki, vi = st.pool_indices(0, b, int(lens[b]))
+        assert check_indices(vi, kept[b][1], st.codebooks[0][1]) > 0.99
+    for loop in range(loops):
+        q = wl.vq_query(w, 0, loop, DEV)
+        out = torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=DEV)
+        st.decode(0, loop, q, out)
+        torch.cuda.synchronize()
+        rel = compare(st, 0, loop, q, out, kept, (0, 1), lens)
+        say(f"  loops {loops} loop {loop}: rel err {rel:.2e}")
