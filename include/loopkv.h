@@ -250,11 +250,16 @@ int loopkv_plan_optimize(int32_t R, int32_t L, const double* damage, double dama
  * loop r's channels at positions 4r..4r+3; its key (value) index is one
  * byte naming the nearest of 256 codewords of group j's key (value)
  * codebook.  R = 4 gives 8 bits per 16 elements = 0.5 bit per element.
- * Codebook (one layer, keys or values): device fp16 [D/4][256][4R].
+ * Codebook (one layer, keys or values): device fp16 [R][256][D/4][4], loop
+ *   r's 4 channels of codeword c of group j at ((r*256 + c)*(D/4) + j)*4,
+ *   so one loop's slices of all codewords are one contiguous block.  The
+ *   joint codeword c of group j is the concatenation over r = 0 .. R-1.
  * Pool: device, head-major like the cell pools: head h of physical page p
  *   at byte (h*num_pages + p) * 2*P*(D/4); inside, P key index rows of D/4
- *   bytes (token-major), then P value index rows of D/4 bytes (group j of
- *   token t: key at t*(D/4) + j, value at (P + t)*(D/4) + j).
+ *   bytes (token-major), then P value index rows of D/4 bytes.  A row is
+ *   XOR-rotated by the token's position: group j of the token at sequence
+ *   position t (in-page slot t mod P) is byte j ^ (t mod (D/4)) of its row
+ *   (key at (t mod P)*(D/4) + (j ^ (t mod D/4)), value P*(D/4) further).
  */
 typedef struct {
   int32_t loops;       /* R, 2..4 */
@@ -275,7 +280,7 @@ size_t loopkv_vq_workspace_bytes(const loopkv_vq_dims* dims, int32_t batch, int3
  * in fp32, ties to the lowest index).
  * k_bf16, v_bf16: device [R][B][n_new][H][D] bfloat16, all loops' keys and
  *   values of tokens seq_lens[b] .. seq_lens[b]+n_new-1, 8-byte aligned.
- * codebook_k / codebook_v: device fp16 [D/4][256][4R], 8-byte aligned.
+ * codebook_k / codebook_v: device fp16 [R][256][D/4][4], 8-byte aligned.
  * Pages for all tokens < seq_lens[b] + n_new must be mapped.
  * Errors: LOOPKV_E_INVAL (bad dims, NULL pointers, n_new < 1, misaligned
  *   inputs, max_pages * P < max_seq_len), LOOPKV_E_HIP.
@@ -289,8 +294,9 @@ int loopkv_vq_append(const loopkv_vq_dims* dims, void* pool, int64_t num_pages,
  * loopkv_vq_decode -- one decode step of loop `loop` over a layer's joint
  * cache: keys and values are the loop's slices (positions 4*loop ..
  * 4*loop+3) of the chosen codewords; o = softmax(sm_scale * q.K^) V^.
- * q_bf16: device [B][H][D] bfloat16 (8-byte aligned); out: device fp32
- * [B][H][D].  A sequence of length 0 produces zeros.  The summation
+ * q_bf16: device [B][H][D] bfloat16 (8-byte aligned); codebooks as for
+ * loopkv_vq_append but 16-byte aligned; out: device fp32 [B][H][D].  A
+ * sequence of length 0 produces zeros.  The summation
  * order is fixed by the launch shape, so repeated calls with the same
  * inputs and workspace size give identical bits.
  * Errors: LOOPKV_E_INVAL, LOOPKV_E_CAPACITY (workspace too small),

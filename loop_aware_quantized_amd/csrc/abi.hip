@@ -577,9 +577,10 @@ int loopkv_vq_decode(const loopkv_vq_dims* d, const void* pool, int64_t num_page
     return fail(LOOPKV_E_INVAL, "vq_decode: bad batch");
   if (static_cast<int64_t>(batch->max_pages) * d->page < batch->max_seq_len)
     return fail(LOOPKV_E_INVAL, "vq_decode: max_pages * page < max_seq_len");
-  if ((reinterpret_cast<uintptr_t>(q_bf16) | reinterpret_cast<uintptr_t>(codebook_k) |
-       reinterpret_cast<uintptr_t>(codebook_v)) % 8 != 0 || reinterpret_cast<uintptr_t>(pool) % 16 != 0)
-    return fail(LOOPKV_E_INVAL, "vq_decode: query / codebooks must be 8-byte and the pool 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(q_bf16) % 8 != 0 ||
+      (reinterpret_cast<uintptr_t>(codebook_k) | reinterpret_cast<uintptr_t>(codebook_v) |
+       reinterpret_cast<uintptr_t>(pool)) % 16 != 0)
+    return fail(LOOPKV_E_INVAL, "vq_decode: the query must be 8-byte, codebooks and pool 16-byte aligned");
   if (workspace_bytes < loopkv_vq_workspace_bytes(d, batch->batch, batch->max_seq_len))
     return fail(LOOPKV_E_CAPACITY, "vq_decode: workspace smaller than loopkv_vq_workspace_bytes");
   if (batch->batch == 0) return LOOPKV_OK;

@@ -331,7 +331,8 @@ VQ_WORKLOADS = {
 
 
 def vq_codebooks(w: VqWorkload, layer: int, device):
-    """(keys, values) codebooks of one layer, fp16 [D/4][256][4R].
+    """(keys, values) codebooks of one layer in the library's layout, fp16
+    [R][256][D/4][4]: loop r's 4 channels of codeword c of group j.
 
     Codebook training is out of scope; the codewords are draws from the
     same loop-redundant model as the data: a shared 4-vector per group plus
@@ -344,8 +345,17 @@ def vq_codebooks(w: VqWorkload, layer: int, device):
         g = _gen(w, device, _P_KV, layer, 100 + kv)
         base = torch.randn(G, 256, 1, 4, generator=g, device=device)
         cw = base + w.loop_noise * torch.randn(G, 256, R, 4, generator=g, device=device)
-        out.append(cw.reshape(G, 256, 4 * R).to(torch.float16).contiguous())
+        out.append(cw.permute(2, 1, 0, 3).to(torch.float16).contiguous())
     return out[0], out[1]
+
+
+def vq_joint_codebook(cb):
+    """Library codebook [R][256][G][4] -> joint codewords [G][256][4R]
+    (loop r's channels at positions 4r .. 4r+3), as a host float64 array."""
+    import numpy as np
+    a = cb.float().cpu().numpy().astype(np.float64)
+    R, C, G, _ = a.shape
+    return a.transpose(2, 1, 0, 3).reshape(G, C, 4 * R)
 
 
 def vq_kv(w: VqWorkload, layer: int, b: int, t0: int, t1: int, device):

@@ -198,4 +198,6 @@ class VqState:
         blk = self.pools[l].view(H, self.num_pages, 2 * P * G).index_select(1, pages).cpu().numpy()
         k = blk[:, :, :P * G].reshape(H, n * P, G)[:, :T].transpose(1, 0, 2)
         v = blk[:, :, P * G:].reshape(H, n * P, G)[:, :T].transpose(1, 0, 2)
-        return k, v
+        # group j of token t is stored at byte j ^ (t mod G) of its row
+        pos = np.arange(G)[None, :] ^ (np.arange(T) % G)[:, None]          # [T][G]
+        return (np.take_along_axis(k, pos[:, None, :], 2), np.take_along_axis(v, pos[:, None, :], 2))

@@ -34,7 +34,7 @@ def bf16_to_f64(bits):
 
 def check_indices(gpu_idx, x_loops_bits, codebook):
     """gpu_idx [T][H][G]; x_loops_bits uint16 [R][T][H][D] -> exact-match fraction."""
-    cb = codebook.float().cpu().numpy().astype(np.float64)
+    cb = wl.vq_joint_codebook(codebook)
     x = bf16_to_f64(x_loops_bits)
     exact = total = 0
     for h in range(x.shape[2]):
@@ -48,8 +48,8 @@ def check_indices(gpu_idx, x_loops_bits, codebook):
     return exact / max(total, 1)
 
 
-def compare(st, l, loop, q, out, kept, seqs, lens):
-    cbk, cbv = (c.float().cpu().numpy().astype(np.float64) for c in st.codebooks[l])
+def compare(st, l, loop, q, out, kept, seqs, lens, sm_scale=1.0):
+    cbk, cbv = (wl.vq_joint_codebook(c) for c in st.codebooks[l])
     qh = bf16_to_f64(wl.bf16_bits(q))
     oh = out.cpu().numpy()
     errs, scale = [], 0.0
@@ -59,7 +59,7 @@ def compare(st, l, loop, q, out, kept, seqs, lens):
         for h in range(st.w.heads):
             k_hat = ov.decode_loop(ki[:, h].astype(np.int64), cbk, loop)
             v_hat = ov.decode_loop(vi[:, h].astype(np.int64), cbv, loop)
-            want = ov.attend(qh[b, h], k_hat, v_hat)
+            want = ov.attend(qh[b, h], k_hat, v_hat, sm_scale)
             errs.append(np.abs(oh[b, h] - want).max())
             scale = max(scale, np.abs(want).max())
     err = max(errs)
@@ -155,3 +155,21 @@ def test_vq_several_splits(loops):
         torch.cuda.synchronize()
         rel = compare(st, 0, loop, q, out, kept, (0, 1), lens)
         say(f"  loops {loops} loop {loop}: rel err {rel:.2e}")
+
+
+@pytest.mark.parametrize("sm_scale", [0.05, 30.0])
+def test_vq_flat_and_peaky_softmax(sm_scale):
+    """A near-uniform softmax and a peaky one whose running maximum rises
+    far above the first scores many times along the sequence."""
+    w = wl.VqWorkload("vq-scale", 14, batch=2, loops=4, layers=1, heads=2, head_dim=128, page=32, ctx=5000)
+    lens = np.array([5000, 700], np.int32)
+    st = runner.VqState(w, DEV, lengths=lens)
+    kept = st.prefill_layer(0)
+    torch.cuda.synchronize()
+    for loop in (0, 3):
+        q = wl.vq_query(w, 0, loop, DEV)
+        out = torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=DEV)
+        st.decode(0, loop, q, out, sm_scale=sm_scale)
+        torch.cuda.synchronize()
+        rel = compare(st, 0, loop, q, out, kept, (0, 1), lens, sm_scale)
+        say(f"  scale {sm_scale} loop {loop}: rel err {rel:.2e}")
