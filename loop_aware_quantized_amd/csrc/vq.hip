@@ -13,6 +13,10 @@
 // layer share one index cache; loop r decodes slice [4r, 4r+4) of each
 // codeword.
 //
+// Codebook layout: [R][256][G][4] fp16 (G = D/4), loop r's 4 channels of
+// codeword c of group j at ((r * 256 + c) * G + j) * 4, so a decode of one
+// loop reads one contiguous slice.
+//
 // Layout of a head-block (one head, one page of P tokens): P key index
 // rows of D/4 bytes, then P value index rows of D/4 bytes (token-major), so
 // the 64 lanes of a wave read one 64-token tile's rows as contiguous runs.
@@ -24,11 +28,11 @@
 //      in LDS, so a token's score is the sum of D/4 table reads addressed by
 //      its key bytes;
 //   2. each wave streams its own 64-token tiles (lane = token) with a
-//      private online softmax: score, wave maximum (accumulators rescaled
-//      only when it rises), p_t, and per value group one LDS read of the 4
-//      fp16 channels of the chosen codeword and 4 FMAs into the lane's D
-//      accumulators;
-//   3. lanes are summed by a butterfly, waves through LDS: (max, sum, o).
+//      per-lane softmax reference: score, p_t, and per value group one LDS
+//      read of the 4 fp16 channels of the chosen codeword and 4 FMAs into
+//      the lane's D accumulators;
+//   3. lanes are brought to the wave's reference and summed by a butterfly,
+//      waves combined through LDS: (max, sum, o).
 // With several splits the partials are merged by the plain log-sum-exp
 // merge; with one the block writes o / sum.
 #include "device.hpp"
