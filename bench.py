@@ -226,14 +226,15 @@ class Bench:
         if args.graph:
             self.capture()
         first = self.step_idx
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record()
+        for i in range(args.steps):
             self.step()
-        ev1.record()
+            evs[i + 1].record()
         torch.cuda.synchronize()
-        total_ms = ev0.elapsed_time(ev1)
+        total_ms = evs[0].elapsed_time(evs[-1])
         ms_per_step = total_ms / args.steps
+        self.step_spread = step_spread(evs)
         # per-kernel durations: library events around every launch of one step
         abi.loopkv_profile_enable(True)
         for c in (abi.KERNEL_SPLIT, abi.KERNEL_MERGE, abi.KERNEL_APPEND):
@@ -270,7 +271,7 @@ class Bench:
         lo_stored = sum(int(self.lens_of(cnt_step).sum()) * H * D // 4
                         for (r, l) in self.order if self.src_kind(r, l) == self.wl.KIND_Q4)
         return {
-            "value": value, "ms_per_step": ms_per_step,
+            "value": value, "ms_per_step": ms_per_step, "step_ms": self.step_spread,
             "hbm_gbs_required": step_gbs, "bytes_required_per_step": step_bytes,
             "split": {"launches": n_split, "ms": split_ms, "alg_bytes": split_alg, "achieved_gbs": achieved},
             "kernels_ms_per_step": {k: v[1] for k, v in kst.items()},
@@ -412,13 +413,14 @@ def vq_main(args, w):
         step()
     torch.cuda.synchronize()
     first = state["s"]
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
         step()
-    e1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    spread = step_spread(evs)
     abi.loopkv_profile_enable(True)
     for c in (abi.KERNEL_SPLIT, abi.KERNEL_MERGE, abi.KERNEL_APPEND):
         abi.loopkv_profile_collect(c)
@@ -448,6 +450,7 @@ def vq_main(args, w):
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "launches": n_split, "avg_launch_us": split_ms * 1e3 / max(n_split, 1)},
         "kernels_ms_per_step": {k: v[1] for k, v in kst.items()},
+        "step_ms": spread,
         "storage": {"stored_bytes": stored},
         "cpu_baseline": None,
     }
@@ -456,6 +459,15 @@ def vq_main(args, w):
         with open(args.report, "w") as f:
             f.write(line + "\n")
     print(line, flush=True)
+
+
+def step_spread(evs):
+    """Median, p10 and p90 of the per-step durations between consecutive
+    events (ms); the events were recorded between steps on the timed stream."""
+    import numpy as np
+    d = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(len(evs) - 1)])
+    return {"median": float(np.median(d)), "p10": float(np.percentile(d, 10)),
+            "p90": float(np.percentile(d, 90))}
 
 
 def main():
@@ -548,6 +560,7 @@ def main():
                      "measured_read_peak": peak,
                      "frac_of_measured_read_peak": sp["achieved_gbs"] / peak},
         "kernels_ms_per_step": primary["kernels_ms_per_step"],
+        "step_ms": primary["step_ms"],
         "lo_plane": primary["lo_plane"],
         "storage": {"stored_bytes": stored_bytes, "all_4bit_bytes": all_q4_bytes,
                     "saving_vs_all_4bit": (1 - stored_bytes / all_q4_bytes) if all_q4_bytes else None},
