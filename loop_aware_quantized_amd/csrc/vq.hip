@@ -46,10 +46,13 @@ constexpr int kSplitWaves = 8;
 constexpr float kSlack = 8.0f;       // decode: a lane's weights stay below e^kSlack
 constexpr int kSplitThreads = 64 * kSplitWaves;
 
-// Encode: one thread per (sequence, new token, head), a block per 256 of
-// them and per channel group (blockIdx.y); blockIdx.z = 0 keys, 1 values.
-// Nearest codeword in squared distance, fp32, ties to the lowest index.
-template <int D, int R>
+// Encode: kSub threads per (sequence, new token, head), a block per
+// 256 / kSub of them and per channel group (blockIdx.y); blockIdx.z = 0
+// keys, 1 values.  Nearest codeword in squared distance, fp32, ties to the
+// lowest index: each of the kSub threads scans 256 / kSub consecutive codes,
+// then the kSub candidates are compared (equal distances: lower code).
+// kSub = 4 when few tokens are coded, so that the grid fills the chip.
+template <int D, int R, int kSub>
 __global__ __launch_bounds__(kThreads) void vq_encode_kernel(VqArgs a) {
   constexpr int G = D / kVqSub;
   constexpr int J = kVqSub * R;
@@ -59,15 +62,21 @@ __global__ __launch_bounds__(kThreads) void vq_encode_kernel(VqArgs a) {
   // codebook [R][256][G][4]: codeword c of group j is loop r's 4 channels at
   // ((r * 256 + c) * G + j) * 4, r = 0 .. R-1
   const uint16_t* cb = is_v ? a.cb_v : a.cb_k;
-  for (int e = threadIdx.x; e < kVqCodes * J; e += kThreads) {
-    const int c = e / J, r = (e % J) / kVqSub, u = e % kVqSub;
-    cw[e] = f16_to_f32(cb[((static_cast<int64_t>(r) * kVqCodes + c) * G + j) * kVqSub + u]);
+  for (int e = threadIdx.x; e < kVqCodes * R; e += kThreads) {     // one (code, loop) slice each
+    const int c = e / R, r = e % R;
+    const uint2 w = *reinterpret_cast<const uint2*>(cb + ((static_cast<int64_t>(r) * kVqCodes + c) * G + j) * kVqSub);
+    float* d = cw + c * J + kVqSub * r;
+    d[0] = f16_to_f32(w.x & 0xffffu);
+    d[1] = f16_to_f32(w.x >> 16);
+    d[2] = f16_to_f32(w.y & 0xffffu);
+    d[3] = f16_to_f32(w.y >> 16);
   }
   __syncthreads();
 
-  const int64_t m = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t m = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kSub;
+  const int sub = threadIdx.x % kSub;
   const int64_t M = static_cast<int64_t>(a.batch) * a.n_new * a.H;
-  if (m >= M) return;
+  if (m >= M) return;                       // the kSub threads of m leave together
   const int h = static_cast<int>(m % a.H);
   const int64_t bi = m / a.H;
   const int i = static_cast<int>(bi % a.n_new);
@@ -85,7 +94,8 @@ __global__ __launch_bounds__(kThreads) void vq_encode_kernel(VqArgs a) {
   }
   float best = INFINITY;
   int best_c = 0;
-  for (int c = 0; c < kVqCodes; ++c) {
+  constexpr int kSpan = kVqCodes / kSub;
+  for (int c = sub * kSpan; c < (sub + 1) * kSpan; ++c) {
     float dist = 0.0f;
 #pragma unroll
     for (int e = 0; e < J; ++e) {
@@ -97,6 +107,16 @@ __global__ __launch_bounds__(kThreads) void vq_encode_kernel(VqArgs a) {
       best_c = c;
     }
   }
+#pragma unroll
+  for (int o = 1; o < kSub; o <<= 1) {
+    const float ob = __shfl_xor(best, o, 64);
+    const int oc = __shfl_xor(best_c, o, 64);
+    if (ob < best || (ob == best && oc < best_c)) {
+      best = ob;
+      best_c = oc;
+    }
+  }
+  if (sub != 0) return;
   const int t = a.seq_lens[b] + i;
   const int32_t page = a.block_tables[static_cast<int64_t>(b) * a.max_pages + t / a.P];
   const int64_t hb = static_cast<int64_t>(2) * a.P * G;
@@ -386,8 +406,14 @@ __global__ __launch_bounds__(kSplitThreads) void vq_split_kernel(VqArgs a) {
 template <int D, int R>
 hipError_t launch_encode_t(const VqArgs& a, hipStream_t stream) {
   const int64_t M = static_cast<int64_t>(a.batch) * a.n_new * a.H;
-  const dim3 grid(static_cast<unsigned>((M + kThreads - 1) / kThreads), D / kVqSub, 2);
-  hipLaunchKernelGGL((vq_encode_kernel<D, R>), grid, dim3(kThreads), 0, stream, a);
+  if (M <= 16384) {                        // few token-heads (a decode step): four threads each
+    constexpr int kPer = kThreads / 4;
+    const dim3 grid(static_cast<unsigned>((M + kPer - 1) / kPer), D / kVqSub, 2);
+    hipLaunchKernelGGL((vq_encode_kernel<D, R, 4>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    const dim3 grid(static_cast<unsigned>((M + kThreads - 1) / kThreads), D / kVqSub, 2);
+    hipLaunchKernelGGL((vq_encode_kernel<D, R, 1>), grid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
