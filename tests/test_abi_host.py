@@ -167,3 +167,64 @@ def test_append_and_decode_reject_bad_host_arguments():
                            k.data_ptr(), out.data_ptr(), ctypes.byref(abi.make_opts(small_ws)), None)
     assert rc == abi.E_INVAL and "source cell pool" in abi.last_error()
     p.close()
+
+
+def _round_up(x, m):
+    return (x + m - 1) // m * m
+
+
+def test_vq_size_queries():
+    """Sizes of the joint-code calls follow their documented layouts."""
+    d = abi.vq_dims(4, 16, 128, 32)
+    assert abi.vq_codebook_bytes(d) == 4 * 256 * 32 * 4 * 2          # [R][256][D/4][4] fp16
+    assert abi.vq_pool_bytes(d, 10) == 16 * 10 * 2 * 32 * 32          # [H][pages]: 2 x P x D/4 bytes
+    assert abi.vq_pool_bytes(d, 0) == 0
+    # partial records of D + 4 floats, at most one split per 512 tokens
+    assert abi.vq_workspace_bytes(d, 3, 1000) == _round_up(3 * 16 * 2 * (128 + 4) * 4, 256)
+    assert abi.vq_workspace_bytes(d, 3, 0) == _round_up(3 * 16 * 1 * (128 + 4) * 4, 256)
+    d64 = abi.vq_dims(2, 2, 64, 16)
+    assert abi.vq_codebook_bytes(d64) == 2 * 256 * 16 * 4 * 2
+    for bad in [(1, 16, 128, 32), (5, 16, 128, 32), (4, 0, 128, 32), (4, 16, 96, 32), (4, 16, 128, 8)]:
+        bd = abi.vq_dims(*bad)
+        assert abi.vq_codebook_bytes(bd) == 0
+        assert abi.vq_pool_bytes(bd, 4) == 0
+        assert abi.vq_workspace_bytes(bd, 1, 64) == 0
+    assert abi.vq_workspace_bytes(d, -1, 64) == 0
+
+
+def test_vq_calls_reject_bad_host_arguments():
+    """Host-visible arguments of loopkv_vq_append / loopkv_vq_decode are
+    validated before anything is launched (addresses below are never used)."""
+    lib = abi.lib()
+    d = abi.vq_dims(4, 2, 128, 32)
+    lens = _FakeTensor(0x7000, shape=(1,))
+    table = _FakeTensor(0x8000, shape=(1, 4))
+    b = abi.make_batch(lens, table, max_seq_len=128)
+    big = abi.make_batch(lens, table, max_seq_len=129)        # 4 pages * 32 < 129
+    none = abi.make_batch(lens, table, max_seq_len=128, batch=0)
+
+    def app(dims=d, pool=0x1000, cbk=0x2000, cbv=0x3000, batch=b, n_new=1, k=0x4000, v=0x5000):
+        return lib.loopkv_vq_append(ctypes.byref(dims), pool, 4, cbk, cbv, ctypes.byref(batch), n_new, k, v, None)
+
+    assert app(dims=abi.vq_dims(5, 2, 128, 32)) == abi.E_INVAL and "loops" in abi.last_error()
+    assert app(dims=abi.vq_dims(4, 2, 128, 12)) == abi.E_INVAL and "page" in abi.last_error()
+    assert app(n_new=0) == abi.E_INVAL
+    assert app(pool=None) == abi.E_INVAL
+    assert app(k=0x4004) == abi.E_INVAL and "aligned" in abi.last_error()
+    assert app(batch=big) == abi.E_INVAL and "max_pages" in abi.last_error()
+    assert app(batch=none) == abi.OK                           # nothing to code
+
+    ws = abi.vq_workspace_bytes(d, 1, 128)
+
+    def dec(loop=0, cbk=0x2000, ws_bytes=ws, batch=b, q=0x6000):
+        return lib.loopkv_vq_decode(ctypes.byref(d), 0x1000, 4, cbk, 0x3000, loop, ctypes.byref(batch), q,
+                                    0x9000, 1.0, 0xA000, ws_bytes, None)
+
+    assert dec(loop=4) == abi.E_INVAL and "loop" in abi.last_error()
+    assert dec(loop=-1) == abi.E_INVAL
+    assert dec(cbk=0x2008) == abi.E_INVAL and "16-byte" in abi.last_error()
+    assert dec(q=0x6004) == abi.E_INVAL
+    assert dec(q=None) == abi.E_INVAL
+    assert dec(ws_bytes=ws - 1) == abi.E_CAPACITY and "workspace" in abi.last_error()
+    assert dec(batch=big) == abi.E_INVAL
+    assert dec(batch=none, ws_bytes=0) == abi.OK               # nothing to decode
