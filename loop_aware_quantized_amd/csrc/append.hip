@@ -8,27 +8,31 @@
 // token over 32 channels, fp16 scale and zero point) after the KIVI entry
 // of the related-papers list on the fugumt LoopVQ page.
 //
-// One 64-lane wave handles one (sequence, head, key group touched by the
-// new tokens).  A key group that already holds tokens is re-quantized over
-// all of them: their raw keys come back from the staging buffer, so the
-// stored cache is a pure function of the token sequence.
+// One block of kAppendThreads threads handles one (sequence, head, key
+// group touched by the new tokens).  A key group that already holds tokens
+// is re-quantized over all of them: their raw keys come back from the
+// staging buffer, so the stored cache is a pure function of the token
+// sequence.
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace lkv {
 namespace {
 
+constexpr int kAppendThreads = 256;
+
 template <int D, int KIND>
-__global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
+__global__ __launch_bounds__(kAppendThreads) void append_pack_kernel(AppendArgs a) {
   constexpr float kLevels = (KIND == kKindQ4) ? 15.0f : 3.0f;
   constexpr int kWords = D / 16;   // 16 two-bit fields per 32-bit word
   constexpr int kNJ = D / kGroup;  // value channel groups
-  constexpr int kRowChunks = D / 8;                   // 16-byte chunks per bf16 key row
-  constexpr int kChunks = kGroup * kRowChunks / 64;   // chunks per lane for a full group
+  constexpr int kRowChunks = D / 8;                               // 16-byte chunks per bf16 key row
+  constexpr int kChunks = kGroup * kRowChunks / kAppendThreads;   // chunks per thread for a full group
+  constexpr int kVT = kGroup / 4;  // threads per value group (4 channels, one packed byte each)
   __shared__ float raw[kGroup][D];
   __shared__ float ks[D], kz[D];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x;     // thread of the block
   const int b = blockIdx.z, h = blockIdx.y;
   const int H = a.H;
   const CellLayout L = a.lay;
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
     uint4 ch[kChunks];
 #pragma unroll
     for (int u = 0; u < kChunks; ++u) {
-      const int c = lane + 64 * u;
+      const int c = lane + kAppendThreads * u;
       const int i = c / kRowChunks, q = c % kRowChunks;
       const int t = gs + i;
       ch[u] = make_uint4(0u, 0u, 0u, 0u);
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < kChunks; ++u) {
-      const int c = lane + 64 * u;
+      const int c = lane + kAppendThreads * u;
       const int i = c / kRowChunks, q = c % kRowChunks;
       if (i < n) {
         const uint32_t w[4] = {ch[u].x, ch[u].y, ch[u].z, ch[u].w};
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
   {
     const int kslot = (gs % L.P) / kGroup;
     uint16_t* km = reinterpret_cast<uint16_t*>(page_of(gs) + L.off_kmeta + kslot * 4 * D);
-    for (int d = lane; d < D; d += 64) {
+    for (int d = lane; d < D; d += kAppendThreads) {
       float mn = raw[0][d], mx = mn;
       for (int i = 1; i < n; ++i) {
         mn = fminf(mn, raw[i][d]);
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
   __syncthreads();
 
   // key codes of every token of the group: one (token, 16-channel word) per task
-  for (int idx = lane; idx < n * kWords; idx += 64) {
+  for (int idx = lane; idx < n * kWords; idx += kAppendThreads) {
     const int i = idx / kWords, k = idx % kWords;
     const int t = gs + i;
     uint32_t whi = 0, wlo = 0;
@@ -131,49 +135,46 @@ __global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
     if (KIND == kKindQ4) reinterpret_cast<uint32_t*>(blk + L.off_klo + r * L.row)[k] = wlo;
   }
 
-  // value codes and metadata of the new tokens: one (token, channel group) per task
+  // value codes and metadata of the new tokens: kVT threads per (token,
+  // channel group), 4 channels each; the group's min and max are combined
+  // over the kVT threads, and each thread writes the byte of its 4 channels
   const int first_new = max(gs, T0);
   const int nv = ge - first_new;
-  for (int idx = lane; idx < nv * kNJ; idx += 64) {
-    const int i = idx / kNJ, j = idx % kNJ;
+  for (int idx = lane; idx < nv * kNJ * kVT; idx += kAppendThreads) {
+    const int part = idx % kVT, task = idx / kVT;
+    const int i = task / kNJ, j = task % kNJ;
     const int t = first_new + i;
-    const uint4* src = reinterpret_cast<const uint4*>(a.v_in + new_row(t) + kGroup * j);
-    float x[kGroup];
+    const uint2 v2 = *reinterpret_cast<const uint2*>(a.v_in + new_row(t) + kGroup * j + 4 * part);
+    const float x[4] = {bf16_to_f32(static_cast<uint16_t>(v2.x & 0xffffu)),
+                        bf16_to_f32(static_cast<uint16_t>(v2.x >> 16)),
+                        bf16_to_f32(static_cast<uint16_t>(v2.y & 0xffffu)),
+                        bf16_to_f32(static_cast<uint16_t>(v2.y >> 16))};
+    float mn = fminf(fminf(x[0], x[1]), fminf(x[2], x[3]));
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
 #pragma unroll
-    for (int e = 0; e < kGroup / 8; ++e) {
-      const uint4 v4 = src[e];
-      const uint32_t w[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        x[8 * e + 2 * f] = bf16_to_f32(static_cast<uint16_t>(w[f] & 0xffffu));
-        x[8 * e + 2 * f + 1] = bf16_to_f32(static_cast<uint16_t>(w[f] >> 16));
-      }
-    }
-    float mn = x[0], mx = x[0];
-#pragma unroll
-    for (int c = 1; c < kGroup; ++c) {
-      mn = fminf(mn, x[c]);
-      mx = fmaxf(mx, x[c]);
+    for (int o = 1; o < kVT; o <<= 1) {     // the kVT threads of a task are adjacent lanes
+      mn = fminf(mn, __shfl_xor(mn, o, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     }
     const QParams q = qparams(mn, mx, kLevels);
-    uint32_t hi[2] = {0, 0}, lo[2] = {0, 0};
+    uint32_t hi = 0, lo = 0;
 #pragma unroll
-    for (int c = 0; c < kGroup; ++c) {
+    for (int c = 0; c < 4; ++c) {
       const uint32_t code = qcode(x[c], q, kLevels);
       if (KIND == kKindQ4) {
-        hi[c / 16] |= (code >> 2) << (2 * (c % 16));
-        lo[c / 16] |= (code & 3u) << (2 * (c % 16));
+        hi |= (code >> 2) << (2 * c);
+        lo |= (code & 3u) << (2 * c);
       } else {
-        hi[c / 16] |= code << (2 * (c % 16));
+        hi |= code << (2 * c);
       }
     }
     const int r = t % L.P;
     uint8_t* blk = page_of(t);
-    *reinterpret_cast<uint2*>(blk + L.off_vhi + r * L.row + 8 * j) = make_uint2(hi[0], hi[1]);
-    if (KIND == kKindQ4)
-      *reinterpret_cast<uint2*>(blk + L.off_vlo + r * L.row + 8 * j) = make_uint2(lo[0], lo[1]);
-    reinterpret_cast<uint32_t*>(blk + L.off_vmeta)[r * kNJ + j] =
-        static_cast<uint32_t>(q.sbits) | (static_cast<uint32_t>(q.zbits) << 16);
+    blk[L.off_vhi + r * L.row + 8 * j + part] = static_cast<uint8_t>(hi);
+    if (KIND == kKindQ4) blk[L.off_vlo + r * L.row + 8 * j + part] = static_cast<uint8_t>(lo);
+    if (part == 0)
+      reinterpret_cast<uint32_t*>(blk + L.off_vmeta)[r * kNJ + j] =
+          static_cast<uint32_t>(q.sbits) | (static_cast<uint32_t>(q.zbits) << 16);
   }
 
   // staging: keep the raw keys of the sequence's open group.  Done here only
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(64) void append_pack_kernel(AppendArgs a) {
   // one-token append); otherwise append_staging_kernel runs afterwards, so
   // no wave overwrites staging rows another wave still reads.
   if (g == g0 && ge == T1 && (T1 % kGroup) != 0) {
-    for (int idx = lane; idx < (ge - first_new) * kRowChunks; idx += 64) {
+    for (int idx = lane; idx < (ge - first_new) * kRowChunks; idx += kAppendThreads) {
       const int i = idx / kRowChunks, q = idx % kRowChunks;
       const int t = first_new + i;
       reinterpret_cast<uint4*>(stg + (t - gs) * D)[q] = reinterpret_cast<const uint4*>(a.k_in + new_row(t))[q];
@@ -216,7 +217,7 @@ template <int D, int KIND>
 hipError_t launch_typed(const AppendArgs& a, int batch, hipStream_t stream) {
   const int groups = (a.n_new + kGroup - 1) / kGroup + 1;
   prof_mark(kClassAppend, 0, stream);
-  hipLaunchKernelGGL((append_pack_kernel<D, KIND>), dim3(groups, a.H, batch), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((append_pack_kernel<D, KIND>), dim3(groups, a.H, batch), dim3(kAppendThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && a.n_new > 1) {
     hipLaunchKernelGGL((append_staging_kernel<D>), dim3(a.H, batch), dim3(64), 0, stream, a);
