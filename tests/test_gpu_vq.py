@@ -173,3 +173,20 @@ def test_vq_flat_and_peaky_softmax(sm_scale):
         torch.cuda.synchronize()
         rel = compare(st, 0, loop, q, out, kept, (0, 1), lens, sm_scale)
         say(f"  scale {sm_scale} loop {loop}: rel err {rel:.2e}")
+
+
+def test_vq_split_length_cap():
+    """Enough sequence-heads to fill the chip with one split each, but
+    sequences longer than the longest split: two splits per sequence-head,
+    the second one short, merged by the log-sum-exp merge."""
+    w = wl.VqWorkload("vq-cap", 15, batch=16, loops=4, layers=1, heads=16, head_dim=128, page=32, ctx=33000)
+    st = runner.VqState(w, DEV)
+    seqs = (0, 15)
+    st.prefill_layer(0)
+    torch.cuda.synchronize()
+    q = wl.vq_query(w, 0, 2, DEV)
+    out = torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=DEV)
+    st.decode(0, 2, q, out)
+    torch.cuda.synchronize()
+    rel = compare(st, 0, 2, q, out, None, seqs, st.lens0)
+    say(f"  33000 tokens, 256 sequence-heads: rel err {rel:.2e}")
