@@ -40,7 +40,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="replay each timed step as one captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-samples", type=int, default=8, help="(cell, sequence) oracle samples")
+    ap.add_argument("--cpu-samples", type=int, default=0,
+                    help="oracle samples: (cell, sequence) decodes, or (layer, loop, sequence) for the joint-code "
+                         "workloads; 0 = about 10 s of single-core work (16, or 40 for joint codes)")
     ap.add_argument("--report", default=None, help="also write the JSON result to this file")
     ap.add_argument("--planner", action="store_true",
                     help="only time the offline plan search (host) and exit")
@@ -437,6 +439,7 @@ def vq_main(args, w):
     n_split, split_ms = kst["split"]
     achieved = split_bytes / (split_ms / 1e3) / 1e9
     stored = L * abi.vq_pool_bytes(st.dims, st.num_pages)
+    cpu = None if args.no_cpu_baseline else vq_cpu_baseline(w, st, queries, n_samples=args.cpu_samples or 40)
     res = {
         "metric": METRIC, "value": tokens * R * L / (ms / 1e3), "unit": "KV tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -452,13 +455,54 @@ def vq_main(args, w):
         "kernels_ms_per_step": {k: v[1] for k, v in kst.items()},
         "step_ms": spread,
         "storage": {"stored_bytes": stored},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     line = json.dumps(res)
     if args.report:
         with open(args.report, "w") as f:
             f.write(line + "\n")
     print(line, flush=True)
+
+
+def vq_cpu_baseline(w, st, queries, n_samples):
+    """Time oracle.loopvq (codeword lookup + float64 attention, all heads) on
+    (layer, loop, sequence) samples of a joint-code workload; the index bytes
+    are copied from the GPU pool first and that copy is not timed."""
+    import oracle.loopvq as ov
+    from loop_aware_quantized_amd import inputs as wl
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    rng = np.random.default_rng(54321)
+    t_total, tokens = 0.0, 0
+    for _ in range(n_samples):
+        l, r, b = int(rng.integers(w.layers)), int(rng.integers(w.loops)), int(rng.integers(w.batch))
+        T = int(st.lens0[b])
+        ki, vi = st.pool_indices(l, b, T)
+        cbk, cbv = (wl.vq_joint_codebook(c) for c in st.codebooks[l])
+        q = (wl.bf16_bits(queries[(r, l)])[b].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+        def run():
+            for h in range(w.heads):
+                ov.attend(q[h], ov.decode_loop(ki[:, h].astype(np.int64), cbk, r),
+                          ov.decode_loop(vi[:, h].astype(np.int64), cbv, r))
+
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                t0 = time.perf_counter()
+                run()
+                t_total += time.perf_counter() - t0
+        else:
+            t0 = time.perf_counter()
+            run()
+            t_total += time.perf_counter() - t0
+        tokens += T
+        log(f"[bench] oracle sample layer {l} loop {r} seq {b}: T={T} cumulative {t_total:.1f} s")
+    return {"value": tokens / t_total, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_samples} (layer, loop, sequence) decodes of {w.name}, all {w.heads} heads, "
+                      f"{tokens} KV tokens, index copy excluded, numpy single thread",
+            "seconds": t_total}
 
 
 def step_spread(evs):
@@ -523,7 +567,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, bench.st, kinds, bench.taus, args.cpu_samples, bench.dev)
+        cpu = cpu_baseline(w, bench.st, kinds, bench.taus, args.cpu_samples or 16, bench.dev)
 
     st = bench.st
     q4_cells = [c for c in st.stored if kinds[c] == wl.KIND_Q4]
