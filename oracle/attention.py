@@ -11,7 +11,7 @@ Sources
     and fetches the low two bits only where that loop's own attention
     weights call for 4-bit precision.
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
 * keys are always read at the source cell's full precision (the weights
   must exist before the mask can be formed): K^ = c*s + z with c = 4*hi + lo
   for a 4-bit source;

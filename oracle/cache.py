@@ -12,7 +12,7 @@ Sources
 * fugumt LoopVQ page, related-papers list, KIVI entry: keys quantized per
   channel over groups of tokens, values per token over groups of channels.
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
 * group size 32; the key group of token t is t // 32 and a trailing partial
   group is quantized over the tokens present, so the cache is a pure
   function of the sequence (appending re-quantizes the open group);

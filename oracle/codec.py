@@ -12,7 +12,7 @@ Sources
 * fugumt LoopVQ page, related-papers list, KIVI entry: asymmetric low-bit
   KV quantization with a per-group floating scale and zero point.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 * zero point z is the group minimum rounded DOWN to fp16, scale s is
   (max - z) / (2^b - 1) computed in fp32 and rounded UP to fp16, so the grid
   z + c*s, c = 0 .. 2^b-1, covers [min, max];

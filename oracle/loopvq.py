@@ -11,7 +11,7 @@ looped model is redundant along the loop axis; LoopVQ codes channels of
 several loop steps jointly with codebooks (fine-tuned in the paper) and
 reaches 0.5 bits per element.
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
 * for one layer, token and head, the joint vector of channel group j is the
   concatenation over loops r = 0..R-1 of channels [4j, 4j+4) of loop r's
   key (or value): 4R numbers;

@@ -10,7 +10,7 @@ up to the model's damage; a one-time offline profile chooses, per cell,
 4-bit storage, 2-bit storage or reuse of the final loop's KV; the planner
 minimizes reads under budgets for predicted damage and storage.
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
 * a plan's damage is the sum of its cells' damages; a cell's damage is the
   profiled value of its kind, and for a reuse cell the value for the format
   its source (the final loop's cell of the layer) is stored in;
