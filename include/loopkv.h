@@ -4,12 +4,12 @@
  *
  * What the library computes comes from "LoopKV: Loop-Aware KV Cache
  * Compression for Serving Looped Transformers", abstract (概要):
- *   - a looped transformer keeps one KV cache per (loop, layer) cell;
- *   - a one-time offline plan stores each cell at 4 bits, at 2 bits, or as a
- *     reuse of the final loop's KV of the same layer;
- *   - while decoding, each loop reads the high two bits of every 4-bit value
- *     and fetches the low two bits only where its own attention weights need
- *     4-bit precision.
+ *   - every (loop, layer) cell of a looped transformer has its own KV cache;
+ *   - a plan fixed ahead of time keeps a cell at 4 bits or at 2 bits, or
+ *     lets it borrow the last loop's cache of the same layer;
+ *   - a decoding loop always uses the upper two bits of a 4-bit value and
+ *     loads the lower two only for tokens whose weight under that loop's own
+ *     query is large enough to need them.
  * The quantizer layout (keys per channel over token groups, values per token
  * over channel groups, fp16 scale and zero point) follows the KIVI entry of
  * the related-papers list on the fugumt LoopVQ page.
@@ -213,10 +213,10 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells,
 /*
  * loopkv_plan_optimize -- offline plan search: the kind of every cell that
  * minimizes decode reads under a damage budget and a storage budget.
- * Source: LoopKV abstract -- single-cell damages add up to the model's
- * damage; a one-time offline profile chooses 4-bit storage, 2-bit storage
- * or reuse of the final loop's KV per cell; the planner minimizes reads
- * under budgets for predicted damage and storage.
+ * Source: LoopKV abstract -- the model's output damage is close to the sum
+ * of per-cell damages; per cell a profile taken once, offline, selects
+ * 4-bit codes, 2-bit codes or borrowing the last loop's cache, and the plan
+ * reads the fewest bytes within limits on predicted damage and storage.
  * damage: host [R][L][4] doubles per cell (loop-major): predicted damage
  *   when the cell is stored at 4 bits, at 2 bits, when it reuses a 4-bit
  *   final-loop cell, when it reuses a 2-bit one (the reuse entries of loop
@@ -242,9 +242,9 @@ int loopkv_plan_optimize(int32_t R, int32_t L, const double* damage, double dama
 /*
  * ---- Joint vector quantization across loop steps (LoopVQ-style) ---------
  * Source: "LoopVQ: Sub 1-bit KV Cache Quantization for Looped
- * Transformers", abstract -- the KV cache of a looped model is redundant
- * along the loop axis; codebooks code channels of several loop steps
- * jointly, at 0.5 bit per element.
+ * Transformers", abstract -- keys and values change little from one loop
+ * step to the next, so one codebook entry stands for a group of channels
+ * of all loop steps at once, at half a bit per element.
  * Format of one layer (all R loops share it): for a token and head, channel
  * group j (channels 4j..4j+3, j < D/4) has a joint vector of 4R numbers,
  * loop r's channels at positions 4r..4r+3; its key (value) index is one

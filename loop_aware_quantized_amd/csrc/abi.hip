@@ -2,10 +2,11 @@
 // parsing and validation, argument checks, split selection and launches.
 //
 // Source of the plan semantics: "LoopKV: Loop-Aware KV Cache Compression for
-// Serving Looped Transformers", abstract (概要) -- one offline decision per
-// (loop, layer) cell among 4-bit storage, 2-bit storage and reuse of the
-// final loop's KV of that layer, with decode-time low-bit fetches decided
-// by the cell's own attention weights (threshold tau per cell).
+// Serving Looped Transformers", abstract (概要) -- a choice made ahead of
+// time for every (loop, layer) cell between 4-bit codes, 2-bit codes and
+// borrowing the last loop's cache of the layer; at decode the lower bits of
+// a 4-bit value are loaded only for tokens whose weight under the cell's
+// own query passes the cell's threshold tau.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

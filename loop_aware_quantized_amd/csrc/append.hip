@@ -2,9 +2,9 @@
 // into its bit-plane paged pool.
 //
 // Source: "LoopKV: Loop-Aware KV Cache Compression for Serving Looped
-// Transformers", abstract (概要) -- cells are stored at 4 or 2 bits, and a
-// 4-bit value is split so that its high two bits can be read without its
-// low two bits.  Group layout (keys per channel over 32 tokens, values per
+// Transformers", abstract (概要) -- a cell keeps 4-bit or 2-bit codes, and a
+// 4-bit code is stored as two 2-bit planes so that the upper one can be
+// read alone.  Group layout (keys per channel over 32 tokens, values per
 // token over 32 channels, fp16 scale and zero point) after the KIVI entry
 // of the related-papers list on the fugumt LoopVQ page.
 //

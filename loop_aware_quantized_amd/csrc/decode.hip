@@ -1,10 +1,10 @@
 // decode.hip -- plan-driven decode attention over one cell's quantized cache.
 //
 // Source: "LoopKV: Loop-Aware KV Cache Compression for Serving Looped
-// Transformers", abstract (概要): each loop reads the high two bits of every
-// 4-bit value and fetches the low two bits only where its own attention
-// weights need 4-bit precision; a cell may instead be 2-bit, or reuse the
-// final loop's cache of its layer.
+// Transformers", abstract (概要): a decoding loop always uses the upper two
+// bits of a 4-bit value and loads the lower two only for tokens whose
+// weight under that loop's own query is large enough to need them; other
+// cells hold 2-bit codes or borrow the last loop's cache of their layer.
 //
 // Two kernels per call:
 //   decode_split_kernel  one wave per (split, head, sequence).  Keys are

@@ -1,8 +1,8 @@
 // layout.hpp -- byte layout of one stored cell's paged pool.
 //
 // Source: "LoopKV: Loop-Aware KV Cache Compression for Serving Looped
-// Transformers", abstract (概要): a cell is stored at 4 or 2 bits, and a
-// 4-bit value's high two bits are read apart from its low two bits, so a
+// Transformers", abstract (概要): a cell keeps 4-bit or 2-bit codes, and
+// the upper two bits of a 4-bit code are used without the lower two, so a
 // 4-bit cell keeps separate high and low planes.  Keys are grouped per
 // channel over 32 tokens and values per token over 32 channels (the KIVI
 // entry of the related-papers list on the fugumt LoopVQ page).

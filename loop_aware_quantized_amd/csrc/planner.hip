@@ -3,10 +3,11 @@
 // damage and storage.
 //
 // Source: "LoopKV: Loop-Aware KV Cache Compression for Serving Looped
-// Transformers", abstract (概要): the damages of single cells add up to the
-// model's damage; a one-time offline profile picks 4-bit storage, 2-bit
-// storage or reuse of the final loop's KV for each cell; the planner
-// minimizes reads under budgets for predicted damage and storage.
+// Transformers", abstract (概要): the model's output damage is close to the
+// sum of per-cell damages; a profile taken once, offline, selects per cell
+// 4-bit codes, 2-bit codes or borrowing the last loop's cache, and the plan
+// reads the fewest bytes while its predicted damage and storage stay within
+// given limits.
 //
 // Host code only.  Exact search: the cells of one layer interact only
 // through reuse (a loop that reuses reads the final loop's cell in that

@@ -2,9 +2,9 @@
 // and the split pass of decode attention over such a cache (LoopVQ-style).
 //
 // Source: "LoopVQ: Sub 1-bit KV Cache Quantization for Looped
-// Transformers", abstract (概要): the KV cache of a looped model is
-// redundant along the loop axis; LoopVQ codes channels of several loop
-// steps jointly with codebooks and reaches 0.5 bit per element.
+// Transformers", abstract (概要): keys and values change little from one
+// loop step to the next, so one codebook entry can stand for a group of
+// channels of all loop steps at once, at half a bit per element.
 //
 // Format: for one layer, token and head, channel group j's joint vector is
 // the concatenation over loops r of channels [4j, 4j+4) of loop r's key (or

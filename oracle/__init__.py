@@ -10,11 +10,11 @@ What it follows (pages cited by title and section; no line numbers):
 
 * "LoopKV: Loop-Aware KV Cache Compression for Serving Looped Transformers",
   abstract (概要 on the mlinfo page, "Full text" on the astralor page):
-  a KV cache kept per (loop, layer) cell; an offline plan gives each cell
-  4-bit storage, 2-bit storage, or reuse of the final loop's KV for that
-  layer; at decode each loop reads the high two bits of every 4-bit value
-  and fetches the low two bits only where its own attention weight needs
-  4-bit precision.
+  every (loop, layer) cell has its own KV cache; a plan fixed ahead of time
+  keeps a cell at 4 bits or at 2 bits, or lets it borrow the last loop's
+  cache of the same layer; a decoding loop always uses the upper two bits
+  of a 4-bit value and loads the lower two only for tokens whose weight,
+  under that loop's own query, is large enough to need them.
 * The related-papers list (関連論文リスト) on the fugumt LoopVQ page, KIVI
   entry: tuning-free asymmetric low-bit KV quantization.  Its layout (keys
   per channel over token groups, values per token over channel groups, with

@@ -6,10 +6,11 @@ Sources
 -------
 * LoopKV abstract ("LoopKV: Loop-Aware KV Cache Compression for Serving
   Looped Transformers", 概要):
-  - each cell is 4-bit, 2-bit, or reuses the final loop's KV of its layer;
-  - during decoding, each loop reads the high two bits of every 4-bit value
-    and fetches the low two bits only where that loop's own attention
-    weights call for 4-bit precision.
+  - a cell holds 4-bit or 2-bit codes, or borrows the last loop's cache of
+    its layer;
+  - at decode the upper two bits of every 4-bit value are used, and the
+    lower two are loaded only for tokens whose weight under the loop's own
+    query is large enough to need them.
 
 Readings where the pages are silent:
 * keys are always read at the source cell's full precision (the weights

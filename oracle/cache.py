@@ -5,10 +5,10 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 Sources
 -------
 * LoopKV abstract ("LoopKV: Loop-Aware KV Cache Compression for Serving
-  Looped Transformers", 概要): one KV cache per (loop, layer) cell; a cell is
-  stored at 4 or 2 bits or reuses the final loop's KV of its layer; decode
-  reads high and low bits of 4-bit values separately, so the two planes of
-  a 4-bit cell live in separate rows.
+  Looped Transformers", 概要): every (loop, layer) cell has its own cache,
+  holding 4-bit or 2-bit codes, or borrowing the last loop's cache of its
+  layer; the upper and lower bit pairs of a 4-bit code are loaded apart, so
+  the two planes of a 4-bit cell live in separate rows.
 * fugumt LoopVQ page, related-papers list, KIVI entry: keys quantized per
   channel over groups of tokens, values per token over groups of channels.
 

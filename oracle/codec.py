@@ -5,10 +5,10 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 Sources
 -------
 * LoopKV abstract ("LoopKV: Loop-Aware KV Cache Compression for Serving
-  Looped Transformers", 概要): cells are stored with 4-bit or 2-bit values,
-  and decode reads the high two bits of a 4-bit value separately from its
-  low two bits.  That fixes the plane split of a 4-bit code c into
-  hi = c >> 2 and lo = c & 3, with c = 4*hi + lo.
+  Looped Transformers", 概要): a cell keeps 4-bit or 2-bit codes, and the
+  upper pair of bits of a 4-bit code must be readable without its lower
+  pair.  Hence the plane split of a 4-bit code c into hi = c >> 2 and
+  lo = c & 3, with c = 4*hi + lo.
 * fugumt LoopVQ page, related-papers list, KIVI entry: asymmetric low-bit
   KV quantization with a per-group floating scale and zero point.
 

@@ -6,10 +6,10 @@ stored fp16 codewords and bf16 inputs, which are exact in float64.
 Source
 ------
 "LoopVQ: Sub 1-bit KV Cache Quantization for Looped Transformers",
-abstract (概要, mlinfo page; also on the fugumt page): the KV cache of a
-looped model is redundant along the loop axis; LoopVQ codes channels of
-several loop steps jointly with codebooks (fine-tuned in the paper) and
-reaches 0.5 bits per element.
+abstract (概要, mlinfo page; also on the fugumt page): keys and values
+change little from one loop step to the next, so one codebook entry can
+stand for a group of channels of all loop steps at once; the paper tunes
+its codebooks and stores half a bit per element.
 
 Readings where the pages are silent:
 * for one layer, token and head, the joint vector of channel group j is the

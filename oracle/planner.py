@@ -5,10 +5,11 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 Source
 ------
 LoopKV abstract ("LoopKV: Loop-Aware KV Cache Compression for Serving
-Looped Transformers", 概要): the damages of single (loop, layer) cells add
-up to the model's damage; a one-time offline profile chooses, per cell,
-4-bit storage, 2-bit storage or reuse of the final loop's KV; the planner
-minimizes reads under budgets for predicted damage and storage.
+Looped Transformers", 概要): the model's output damage is close to the sum
+of the damages measured cell by cell; per cell, a profile taken once and
+offline selects 4-bit codes, 2-bit codes or borrowing the last loop's
+cache, and the plan is the one with the fewest bytes read whose predicted
+damage and storage stay within given limits.
 
 Readings where the pages are silent:
 * a plan's damage is the sum of its cells' damages; a cell's damage is the
