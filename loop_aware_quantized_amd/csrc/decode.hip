@@ -24,10 +24,12 @@
 // An unfetched 4-bit value is (4*hi + 3/2)*s + z, so a flagged token adds
 // p_t * s * (lo - 3/2).
 //
-// Arithmetic: a 2-bit field at bit 2i of a byte is masked in place (byte
-// value code * 4^i) and converted with one byte-to-float conversion; the
-// 4^-i factor is folded into the per-channel multiplier, which keeps the
-// products bit-identical to code * multiplier.
+// Arithmetic: key fields are masked in place inside 16-bit halves, where
+// they read as fp16 subnormals code * 2^k * 2^-24; a mixed-precision FMA
+// widens them as it multiplies, and the 2^24 * 2^-k is folded into the
+// per-channel multiplier, so every product is exactly code * multiplier.
+// Value fields take the same form in packed fp16 dot products (two tokens
+// per instruction); the tau = 0 path converts bytes through fp8.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -60,18 +62,6 @@ __device__ __forceinline__ void cvt_bytes(uint32_t w, float* f) {
   f[0] = lo[0]; f[1] = lo[1]; f[2] = hi[0]; f[3] = hi[1];
 }
 
-// Unpacks one 32-bit word of 16 two-bit fields (channel 4b + i in bits
-// [8b + 2i, 8b + 2i + 1]) into 16 floats in "position" order p = 4i + b.
-// Positions with odd i come out multiplied by 4 (field left in bits 2-3 of
-// its byte); multipliers compensate with plain_factor.
-__device__ __forceinline__ void unpack_plain(uint32_t w, float* f) {
-  const uint32_t u = w >> 4;
-  cvt_bytes(w & 0x03030303u, f);
-  cvt_bytes(w & 0x0C0C0C0Cu, f + 4);
-  cvt_bytes(u & 0x03030303u, f + 8);
-  cvt_bytes(u & 0x0C0C0C0Cu, f + 12);
-}
-
 // Unpacks a high-plane word and a low-plane word into 16 four-bit codes
 // 4*hi + lo as floats, in the same position order p = 4i + b.
 __device__ __forceinline__ void unpack_combined(uint32_t h, uint32_t l, float* f) {
@@ -85,11 +75,53 @@ __device__ __forceinline__ void unpack_combined(uint32_t h, uint32_t l, float* f
   cvt_bytes((o >> 4) & 0x0F0F0F0Fu, f + 12);
 }
 
-// channel (within a 16-channel word) of position p, and its multiplier for
-// plain 2-bit fields (odd i arrive times 4)
+// Key words as pairs of fp16 halves.  A 2-bit field (or a 4-bit code)
+// masked in place inside a 16-bit half is an fp16 subnormal
+// code * 2^k * 2^-24 (exact), which a mixed-precision FMA widens to fp32
+// as it multiplies; the 2^24 * 2^-k lands in the channel's multiplier.
+// pr[2i] holds field i of bytes 0 and 2, pr[2i + 1] field i of bytes 1
+// and 3 (read from w >> 6, so they arrive times 4).
+__device__ __forceinline__ void key_pairs_plain(uint32_t w, uint32_t* pr) {
+  const uint32_t u = w >> 6;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pr[2 * i] = w & (0x00030003u << (2 * i));
+    pr[2 * i + 1] = u & (0x000C000Cu << (2 * i));
+  }
+}
+
+// The same for 4-bit codes 4*hi + lo built from a high-plane and a
+// low-plane word: even fields as the low nibbles of e, odd ones of o; the
+// nibble of fields 2 and 3 arrives times 16.
+__device__ __forceinline__ void key_pairs_combined(uint32_t h, uint32_t l, uint32_t* pr) {
+  const uint32_t e = ((h << 2) & 0xCCCCCCCCu) | (l & 0x33333333u);
+  const uint32_t o = (h & 0xCCCCCCCCu) | ((l >> 2) & 0x33333333u);
+  const uint32_t e6 = e >> 6, o6 = o >> 6;
+  pr[0] = e & 0x000F000Fu; pr[1] = e6 & 0x003C003Cu;   // field 0
+  pr[2] = o & 0x000F000Fu; pr[3] = o6 & 0x003C003Cu;   // field 1
+  pr[4] = e & 0x00F000F0u; pr[5] = e6 & 0x03C003C0u;   // field 2
+  pr[6] = o & 0x00F000F0u; pr[7] = o6 & 0x03C003C0u;   // field 3
+}
+
+__device__ __forceinline__ float half_lo(uint32_t x) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(x)));
+}
+__device__ __forceinline__ float half_hi(uint32_t x) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(x >> 16)));
+}
+
+// channel (within a 16-channel word) of position p = 4i + b (field i of
+// byte b), and back
 __host__ __device__ constexpr int pos_channel(int p) { return 4 * (p % 4) + p / 4; }
 __host__ __device__ constexpr int channel_pos(int m) { return 4 * (m % 4) + m / 4; }
-__device__ __forceinline__ constexpr float plain_factor(int p) { return ((p / 4) & 1) ? 0.25f : 1.0f; }
+// multiplier factor of key position p: undoes the 2^-24 of the subnormal
+// and the 2^k at which the field sits in its half
+template <bool kCombined>
+__device__ __forceinline__ constexpr float key_factor(int p) {
+  const int i = p / 4, odd_byte = p & 1;
+  return kCombined ? 16777216.0f / static_cast<float>(1 << (4 * (i / 2) + 2 * odd_byte))
+                   : 16777216.0f / static_cast<float>(1 << (2 * (i + odd_byte)));
+}
 // value position p = 4i + b accumulated as fp16 subnormals code * 4^i * 2^-24
 __device__ __forceinline__ constexpr float dot2_factor(int p) {
   return 16777216.0f / static_cast<float>(1 << (2 * (p / 4)));
@@ -500,8 +532,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         const float qv = qs[d];
         bpart = fmaf(qv, z, bpart);
         const int pos = (d & ~15) + channel_pos(d & 15);
-        const float f = kKeyComb ? inv_unit : inv_unit * plain_factor(pos & 15);
-        qk[gsel][pos] = gvalid ? qv * s * f : 0.0f;
+        qk[gsel][pos] = gvalid ? qv * s * key_factor<kKeyComb>(pos & 15) : 0.0f;
       }
       const float rs = row_sum(gvalid ? bpart : 0.0f);
       bias0 = lane_f(rs, 0) + lane_f(rs, 16);
@@ -520,20 +551,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < kWords; ++k) {
         const uint32_t hw = (&cur.kh[k / 4].x)[k % 4];
-        float f[16];
+        uint32_t pr[8];
         if (kKeyComb) {
           const uint32_t lw = (&cur.kl[k / 4].x)[k % 4];
-          unpack_combined(hw, lw, f);
+          key_pairs_combined(hw, lw, pr);
         } else {
-          unpack_plain(hw, f);
+          key_pairs_plain(hw, pr);
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
+          // positions 4v + b of this word: bytes 0, 1, 2, 3 of field v
           const float4 q4 = qv4[4 * k + v];
-          dot = fmaf(q4.x, f[4 * v], dot);
-          dot = fmaf(q4.y, f[4 * v + 1], dot);
-          dot = fmaf(q4.z, f[4 * v + 2], dot);
-          dot = fmaf(q4.w, f[4 * v + 3], dot);
+          dot = fmaf(half_lo(pr[2 * v]), q4.x, dot);
+          dot = fmaf(half_lo(pr[2 * v + 1]), q4.y, dot);
+          dot = fmaf(half_hi(pr[2 * v]), q4.z, dot);
+          dot = fmaf(half_hi(pr[2 * v + 1]), q4.w, dot);
         }
         // keep each word's multiplier reads next to their use (register pressure)
         asm volatile("" ::: "memory");

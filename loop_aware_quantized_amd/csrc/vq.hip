@@ -148,7 +148,6 @@ __global__ __launch_bounds__(kThreads) void vq_encode_kernel(VqArgs a) {
 template <int D, int R>
 __global__ __launch_bounds__(kSplitThreads) void vq_split_kernel(VqArgs a) {
   constexpr int G = D / kVqSub;          // groups = index bytes per row (16 or 32)
-  constexpr int J = kVqSub * R;
   constexpr int kWords = G / 16;         // 16-byte words per index row
   constexpr int kKeyCols = 64;           // 4-byte key-table columns per code (256 B)
   constexpr int kValCols = 32;           // 8-byte value-table columns per code (256 B)
