@@ -200,10 +200,13 @@ typedef struct {
  * own weight p_t >= tau of the calling cell.  An unfetched 4-bit value is
  * reconstructed at its bucket centre (4*hi + 3/2)*s + z.
  * q_bf16: device [B][H][D] bfloat16.  out: device [B][H][D] float32.
- * A sequence of length 0 produces zeros.
+ * A sequence of length 0 produces zeros.  A (sequence, head) is cut into
+ * at most 2048 splits of at most 4096 tokens, so max_seq_len is limited to
+ * 8,388,608.
  * Errors: LOOPKV_E_INVAL (bad cell, NULL pointers, num_splits < 0,
- *   max_pages * P < max_seq_len), LOOPKV_E_CAPACITY (workspace too small),
- *   LOOPKV_E_HIP.
+ *   max_pages * P < max_seq_len, more than 2048 splits, which a
+ *   max_seq_len above the limit or a large num_splits asks for),
+ *   LOOPKV_E_CAPACITY (workspace too small), LOOPKV_E_HIP.
  */
 int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells,
                   int loop, int layer, const loopkv_batch* batch,

@@ -96,9 +96,10 @@ struct Splits {
 //    splits the same length;
 //  - ragged lengths: about three rounds of non-empty splits, so that waves
 //    that finish early pick up the remaining ones and the tail is short.
-// Automatic splits hold at least 256 tokens (4 tiles); a requested count
-// gives splits of ceil(t_max / count) tokens rounded up to a tile.  No split
-// exceeds kMaxSplitLen.
+// Automatic splits hold at least 256 tokens (4 tiles), and long sequences
+// over few pairs get longer splits so that no pair has more than
+// kMaxSplits; a requested count gives splits of ceil(t_max / count) tokens
+// rounded up to a tile.  No split exceeds kMaxSplitLen.
 Splits choose_splits(int64_t batch, int64_t heads, int t_max, int64_t t_sum, int requested) {
   const int64_t tm = std::max<int64_t>(t_max, 1);
   const int64_t pairs = std::max<int64_t>(batch * heads, 1);
@@ -116,6 +117,8 @@ Splits choose_splits(int64_t batch, int64_t heads, int t_max, int64_t t_sum, int
     len = round_up((tm + s0 - 1) / s0, lkv::kTile);
   }
   len = std::max<int64_t>(len, std::min<int64_t>(256, round_up(tm, lkv::kTile)));
+  // long sequences over few pairs: no more than kMaxSplits splits per pair
+  len = std::max<int64_t>(len, round_up((tm + lkv::kMaxSplits - 1) / lkv::kMaxSplits, lkv::kTile));
   len = std::min<int64_t>(len, lkv::kMaxSplitLen);
   const int64_t S = (tm + len - 1) / len;
   return {static_cast<int>(S), static_cast<int>(len)};

@@ -157,6 +157,23 @@ def test_near_uniform_batch_vs_one_split():
         assert rel < 1e-3
 
 
+@pytest.mark.timeout(300)
+def test_long_sequence_few_pairs():
+    """A 600K-token sequence over two (sequence, head) pairs: the automatic
+    layout would want more than the 2048 splits a pair may have, so splits
+    grow instead.  A tau near 1/T flags many tokens (long candidate lists,
+    several gather passes).  The oracle side takes about half a minute."""
+    lens = [600_003, 1000]
+    w = wl.Workload("long", 210, batch=2, loops=1, layers=1, heads=1, head_dim=128, page=64,
+                    ctx=max(lens), heavy_frac=0.0)
+    st = runner.CacheState(w, DEV, [[Q4]], [[1e-6]], lengths=lens)
+    kept = st.prefill({c: {0, 1} for c in st.stored})
+    q, out, mask, cnt = _decode(st, 0, 0)
+    s = compare_decode(st, 0, 0, q, out, mask, kept[(0, 0)], [0, 1])
+    say(f"  rel err {s['rel']:.2e} flagged {s['flagged']} band {s['band']}")
+    assert s["flagged"] > 1000
+
+
 def test_graph_replay_matches_eager():
     """Appends and decodes captured in one HIP graph give, on every replay,
     the same bytes as the same calls made eagerly (eager work and
