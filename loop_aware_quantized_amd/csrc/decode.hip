@@ -182,12 +182,31 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   uint32_t* mrow = a.mask_bits ? a.mask_bits + pair * a.mask_words : nullptr;
 
   // --- log-sum-exp merge: lanes over splits for (max, sum); lanes over
-  //     channels for o, each split's weight broadcast from its lane
-  float M = -INFINITY;
-  for (int i = lane; i < S_used; i += 64) M = fmaxf(M, parts[i * kRec]);
+  //     channels for o, each split's weight broadcast from its lane.  The
+  //     (max, sum) of the first 64 splits, their first eight records and
+  //     (sparse) their candidate counts are requested together, so with up
+  //     to eight splits the merge waits for the partials once.
+  float m_l = -INFINITY, l_l = 0.0f;
+  if (lane < S_used) {
+    const float2 ml = *reinterpret_cast<const float2*>(parts + lane * kRec);
+    m_l = ml.x;
+    l_l = ml.y;
+  }
+  const int cnt0 = (kSparse && lane < S_used) ? a.cand_count[pair * a.S + lane] : 0;
+  float v0[8][kCPL];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    // records past S_used re-read record 0 (their weight is 0): no branches
+    const float* rec = parts + (u < S_used ? u : 0) * kRec + kPartialPad;
+#pragma unroll
+    for (int c = 0; c < kCPL; ++c) v0[u][c] = rec[lane + 64 * c];
+  }
+  float M = m_l;
+  for (int i = lane + 64; i < S_used; i += 64) M = fmaxf(M, parts[i * kRec]);
   M = wave_max(M);
-  float lsum = 0.0f;
-  for (int i = lane; i < S_used; i += 64) lsum = fmaf(__expf(parts[i * kRec] - M), parts[i * kRec + 1], lsum);
+  const float e0 = lane < S_used ? __expf(m_l - M) : 0.0f;   // weight of split `lane`
+  float lsum = e0 * l_l;
+  for (int i = lane + 64; i < S_used; i += 64) lsum = fmaf(__expf(parts[i * kRec] - M), parts[i * kRec + 1], lsum);
   lsum = wave_sum(lsum);
   const float inv = 1.0f / lsum;
   const float lse = M + logf(lsum);
@@ -195,11 +214,17 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     float o[kCPL];
 #pragma unroll
     for (int c = 0; c < kCPL; ++c) o[c] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float e = lane_f(e0, u);   // 0 past S_used
+#pragma unroll
+      for (int c = 0; c < kCPL; ++c) o[c] = fmaf(e, v0[u][c], o[c]);
+    }
     for (int i0 = 0; i0 < S_used; i0 += 64) {
       const int n = min(64, S_used - i0);
-      const float e_l = lane < n ? __expf(parts[(i0 + lane) * kRec] - M) : 0.0f;
+      const float e_l = i0 == 0 ? e0 : (lane < n ? __expf(parts[(i0 + lane) * kRec] - M) : 0.0f);
       // eight records per step, all loads issued before the first use
-      for (int j = 0; j < n; j += 8) {
+      for (int j = i0 == 0 ? 8 : 0; j < n; j += 8) {
         float v[8][kCPL];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -274,7 +299,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     // over the inclusive prefix of the list lengths.
     for (int i0 = 0; i0 < S_used; i0 += 64) {
       const int ns = min(64, S_used - i0);
-      const int cnt = lane < ns ? a.cand_count[pair * a.S + i0 + lane] : 0;
+      const int cnt = i0 == 0 ? cnt0 : (lane < ns ? a.cand_count[pair * a.S + i0 + lane] : 0);
       int incl = cnt;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
