@@ -155,6 +155,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int kRec = D + kPartialPad;
   constexpr int kCPL = D / 64;           // output channels per lane
   constexpr int kPass = 4;               // candidates per lane per scan pass
+  constexpr int kFirst = 16;             // records requested with the length
   constexpr bool kSparse = MODE == kModeSparse;
   constexpr bool kDense = MODE == kModeDense;
   static_assert(kFlagCap >= 2 * 64 * kPass, "flag buffer must hold two scan passes");
@@ -168,39 +169,39 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int lane = threadIdx.x;
   const int h = blockIdx.x, b = blockIdx.y;
   const CellLayout L = a.lay;
-  const int T = a.seq_lens[b];
   const int64_t pair = static_cast<int64_t>(b) * a.H + h;
   float* outp = a.out + pair * D;
+  const float* parts = a.partials + pair * a.S * kRec;
+
+  // --- log-sum-exp merge: lanes over splits for (max, sum); lanes over
+  //     channels for o, each split's weight broadcast from its lane.  The
+  //     (max, sum) of the first 64 split slots, the first kFirst records and
+  //     (sparse) the candidate counts are requested together with the
+  //     length, so with up to kFirst splits the merge waits for memory once.
+  //     Slots past the sequence's splits hold stale values; they are masked
+  //     once the length is known.
+  float2 ml_raw = make_float2(-INFINITY, 0.0f);
+  if (lane < a.S) ml_raw = *reinterpret_cast<const float2*>(parts + lane * kRec);
+  const int cnt_raw = (kSparse && lane < a.S) ? a.cand_count[pair * a.S + lane] : 0;
+  float v0[kFirst][kCPL];
+#pragma unroll
+  for (int u = 0; u < kFirst; ++u) {
+    const float* rec = parts + (u < a.S ? u : 0) * kRec + kPartialPad;
+#pragma unroll
+    for (int c = 0; c < kCPL; ++c) v0[u][c] = rec[lane + 64 * c];
+  }
+  const int T = a.seq_lens[b];
   if (T <= 0) {
     for (int d = lane; d < D; d += 64) outp[d] = 0.0f;
     return;
   }
   // lengths above max_seq_len break the caller's contract; never read past S
   const int S_used = min((T + a.split_len - 1) / a.split_len, a.S);
-  const float* parts = a.partials + pair * a.S * kRec;
   // the row was cleared by the split kernel (first split of the pair)
   uint32_t* mrow = a.mask_bits ? a.mask_bits + pair * a.mask_words : nullptr;
-
-  // --- log-sum-exp merge: lanes over splits for (max, sum); lanes over
-  //     channels for o, each split's weight broadcast from its lane.  The
-  //     (max, sum) of the first 64 splits, their first eight records and
-  //     (sparse) their candidate counts are requested together, so with up
-  //     to eight splits the merge waits for the partials once.
-  float m_l = -INFINITY, l_l = 0.0f;
-  if (lane < S_used) {
-    const float2 ml = *reinterpret_cast<const float2*>(parts + lane * kRec);
-    m_l = ml.x;
-    l_l = ml.y;
-  }
-  const int cnt0 = (kSparse && lane < S_used) ? a.cand_count[pair * a.S + lane] : 0;
-  float v0[8][kCPL];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    // records past S_used re-read record 0 (their weight is 0): no branches
-    const float* rec = parts + (u < S_used ? u : 0) * kRec + kPartialPad;
-#pragma unroll
-    for (int c = 0; c < kCPL; ++c) v0[u][c] = rec[lane + 64 * c];
-  }
+  const float m_l = lane < S_used ? ml_raw.x : -INFINITY;
+  const float l_l = lane < S_used ? ml_raw.y : 0.0f;
+  const int cnt0 = lane < S_used ? cnt_raw : 0;
   float M = m_l;
   for (int i = lane + 64; i < S_used; i += 64) M = fmaxf(M, parts[i * kRec]);
   M = wave_max(M);
@@ -215,16 +216,16 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < kCPL; ++c) o[c] = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float e = lane_f(e0, u);   // 0 past S_used
+    for (int u = 0; u < kFirst; ++u) {
+      const float e = lane_f(e0, u);
 #pragma unroll
-      for (int c = 0; c < kCPL; ++c) o[c] = fmaf(e, v0[u][c], o[c]);
+      for (int c = 0; c < kCPL; ++c) o[c] = u < S_used ? fmaf(e, v0[u][c], o[c]) : o[c];   // stale past S_used
     }
     for (int i0 = 0; i0 < S_used; i0 += 64) {
       const int n = min(64, S_used - i0);
       const float e_l = i0 == 0 ? e0 : (lane < n ? __expf(parts[(i0 + lane) * kRec] - M) : 0.0f);
       // eight records per step, all loads issued before the first use
-      for (int j = i0 == 0 ? 8 : 0; j < n; j += 8) {
+      for (int j = i0 == 0 ? kFirst : 0; j < n; j += 8) {
         float v[8][kCPL];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -403,6 +404,29 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int end = min(start + a.split_len, T);
   const int64_t pair = static_cast<int64_t>(b) * H + h;
   float* part = a.partials + (pair * a.S + split) * (D + kPartialPad);
+  // page size is a power of two; splits and tiles start on page boundaries
+  const int lgP = __builtin_ctz(static_cast<unsigned>(L.P));
+  const int pmask = L.P - 1;
+  // The block-table slice of the split's whole span (clamped to the row)
+  // and the query are requested before the length is known, so that their
+  // reads overlap the length's; entries past the sequence are dropped below.
+  constexpr int kPgSlots = kMaxSplitLen / 16 + 4;
+  constexpr int kPgPerLane = (kPgSlots + 63) / 64;
+  uint32_t pg_raw[kPgPerLane];
+  {
+    const int first = start >> lgP;
+    const int span = min((a.split_len + pmask) >> lgP, a.max_pages - first);
+    const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_pages + first;
+#pragma unroll
+    for (int k = 0; k < kPgPerLane; ++k) {
+      const int i = lane + 64 * k;
+      pg_raw[k] = i < span ? static_cast<uint32_t>(bt[i]) : 0u;
+    }
+  }
+  float q_raw[D / 64];
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) q_raw[c] = bf16_to_f32(a.q[pair * D + lane + 64 * c]);
+
   if (split == 0 && a.mask_bits) {
     // the first split owns the pair's mask row: cleared here (all ones up to
     // T for tau = 0); the merge kernel, launched after, sets the flag bits
@@ -418,16 +442,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
   if (start >= end) return;   // splits past the end take no part in the merge
 
-  // page size is a power of two; splits and tiles start on page boundaries
-  const int lgP = __builtin_ctz(static_cast<unsigned>(L.P));
-  const int pmask = L.P - 1;
   {
-    const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_pages + (start >> lgP);
-    const int np = ((end - start) + pmask) >> lgP;
-    for (int i = lane; i < kMaxSplitLen / 16 + 4; i += 64)
-      pgoff[i] = i < np ? static_cast<uint32_t>(bt[i]) * static_cast<uint32_t>(L.HB) : 0u;
+    const int np = ((end - start) + pmask) >> lgP;   // <= span: end <= T <= max_pages * P
+#pragma unroll
+    for (int k = 0; k < kPgPerLane; ++k) {
+      const int i = lane + 64 * k;
+      if (i < kPgSlots) pgoff[i] = i < np ? pg_raw[k] * static_cast<uint32_t>(L.HB) : 0u;
+    }
   }
-  for (int d = lane; d < D; d += 64) qs[d] = bf16_to_f32(a.q[pair * D + d]) * a.sm_scale;
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) qs[lane + 64 * c] = q_raw[c] * a.sm_scale;
   __syncthreads();
 
   // this head's pool region as a raw buffer: 32-bit offsets, and loads past
