@@ -136,9 +136,11 @@ typedef struct {
   int32_t reserved;
 } loopkv_cell_mem;
 
-/* One batch of sequences.  Every cell uses the same page mapping. */
+/* One batch of sequences.  Every cell uses the same page mapping.  The
+ * device arrays are int32 and must be 4-byte aligned; every call rejects a
+ * batch above 65535 sequences (LOOPKV_E_INVAL). */
 typedef struct {
-  int32_t batch;                /* number of sequences B >= 0                */
+  int32_t batch;                /* number of sequences, 0 <= B <= 65535      */
   int32_t max_pages;            /* row stride of block_tables                */
   const int32_t* seq_lens;      /* device [B]: append = length BEFORE the
                                    append; decode = tokens attended          */
@@ -169,9 +171,9 @@ typedef struct {
  *   be finite with |x| <= 32768.
  * Returns LOOPKV_NOOP_REUSE (nothing launched) for a reuse cell.
  * Errors: LOOPKV_E_INVAL (bad cell, NULL pool/staging, n_new < 1,
- *   misaligned inputs,
- *   batch > max_slots when slots == NULL, max_pages * P < max_seq_len),
- *   LOOPKV_E_HIP.
+ *   misaligned inputs or batch arrays, batch above 65535,
+ *   max_pages * P < max_seq_len), LOOPKV_E_CAPACITY (batch > max_slots
+ *   when slots == NULL), LOOPKV_E_HIP.
  */
 int loopkv_append(const loopkv_plan* plan, const loopkv_cell_mem* cells,
                   int loop, int layer, const loopkv_batch* batch,
@@ -203,7 +205,9 @@ typedef struct {
  * A sequence of length 0 produces zeros.  A (sequence, head) is cut into
  * at most 2048 splits of at most 4096 tokens, so max_seq_len is limited to
  * 8,388,608.
- * Errors: LOOPKV_E_INVAL (bad cell, NULL pointers, num_splits < 0,
+ * Alignment: q 2 bytes, out and mask_bits 4 bytes, counters 8 bytes.
+ * Errors: LOOPKV_E_INVAL (bad cell, NULL pointers, misaligned pointers,
+ *   batch above 65535, num_splits < 0, sm_scale not finite,
  *   max_pages * P < max_seq_len, more than 2048 splits, which a
  *   max_seq_len above the limit or a large num_splits asks for),
  *   LOOPKV_E_CAPACITY (workspace too small), LOOPKV_E_HIP.
@@ -286,7 +290,8 @@ size_t loopkv_vq_workspace_bytes(const loopkv_vq_dims* dims, int32_t batch, int3
  * codebook_k / codebook_v: device fp16 [R][256][D/4][4], 8-byte aligned.
  * Pages for all tokens < seq_lens[b] + n_new must be mapped.
  * Errors: LOOPKV_E_INVAL (bad dims, NULL pointers, n_new < 1, misaligned
- *   inputs, max_pages * P < max_seq_len), LOOPKV_E_HIP.
+ *   inputs or batch arrays, batch above 65535, max_pages * P <
+ *   max_seq_len), LOOPKV_E_HIP.
  */
 int loopkv_vq_append(const loopkv_vq_dims* dims, void* pool, int64_t num_pages,
                      const void* codebook_k, const void* codebook_v,
@@ -302,8 +307,9 @@ int loopkv_vq_append(const loopkv_vq_dims* dims, void* pool, int64_t num_pages,
  * sequence of length 0 produces zeros.  The summation
  * order is fixed by the launch shape, so repeated calls with the same
  * inputs and workspace size give identical bits.
- * Errors: LOOPKV_E_INVAL, LOOPKV_E_CAPACITY (workspace too small),
- *   LOOPKV_E_HIP.
+ * Errors: LOOPKV_E_INVAL (bad dims or loop, NULL or misaligned pointers,
+ *   batch above 65535, sm_scale not finite, max_pages * P < max_seq_len),
+ *   LOOPKV_E_CAPACITY (workspace too small), LOOPKV_E_HIP.
  */
 int loopkv_vq_decode(const loopkv_vq_dims* dims, const void* pool, int64_t num_pages,
                      const void* codebook_k, const void* codebook_v, int loop,

@@ -85,6 +85,21 @@ int cu_count() {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+bool misaligned(const void* p, uintptr_t align) { return (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0; }
+
+// sequences per call: the launch grids carry the batch in a dimension of at
+// most 65535 blocks
+constexpr int32_t kMaxBatch = 65535;
+
+// Host-checkable properties of a batch descriptor that every call shares
+// (NULL pointers and lengths are checked by the callers).
+const char* batch_error(const loopkv_batch* b) {
+  if (b->batch > kMaxBatch) return "batch must be <= 65535";
+  if (misaligned(b->seq_lens, 4) || misaligned(b->slots, 4) || misaligned(b->block_tables, 4))
+    return "seq_lens, slots and block_tables must be 4-byte aligned";
+  return nullptr;
+}
+
 // Split plan for `pairs` (sequence, head) pairs of at most t_max tokens.
 struct Splits {
   int S, len;
@@ -367,6 +382,7 @@ int loopkv_append(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
   if (static_cast<uint64_t>(mem.num_pages) * lkv::make_layout(plan->kind[c], plan->P, plan->D).HB > 0xFFFFFFFFull)
     return fail(LOOPKV_E_INVAL, "append: one head's pool region (num_pages * head-block bytes) exceeds 4 GiB");
   if (batch->batch < 0) return fail(LOOPKV_E_INVAL, "append: negative batch");
+  if (const char* be = batch_error(batch)) return fail(LOOPKV_E_INVAL, std::string("append: ") + be);
   if (n_new < 1) return fail(LOOPKV_E_INVAL, "append: n_new must be >= 1");
   if (batch->batch == 0) return LOOPKV_OK;
   if (!k_bf16 || !v_bf16) return fail(LOOPKV_E_INVAL, "append: NULL key or value input");
@@ -421,10 +437,15 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
   if (static_cast<uint64_t>(mem.num_pages) * lkv::make_layout(src_kind, plan->P, plan->D).HB > 0xFFFFFFFFull)
     return fail(LOOPKV_E_INVAL, "decode: one head's pool region (num_pages * head-block bytes) exceeds 4 GiB");
   if (batch->batch < 0) return fail(LOOPKV_E_INVAL, "decode: negative batch");
+  if (const char* be = batch_error(batch)) return fail(LOOPKV_E_INVAL, std::string("decode: ") + be);
   if (opts->num_splits < 0) return fail(LOOPKV_E_INVAL, "decode: num_splits must be >= 0");
   if (batch->max_seq_len < 0) return fail(LOOPKV_E_INVAL, "decode: negative max_seq_len");
+  if (!std::isfinite(opts->sm_scale)) return fail(LOOPKV_E_INVAL, "decode: sm_scale must be finite");
   if (batch->batch == 0) return LOOPKV_OK;
   if (!q_bf16 || !out) return fail(LOOPKV_E_INVAL, "decode: NULL query or output");
+  if (misaligned(q_bf16, 2) || misaligned(out, 4) || misaligned(opts->mask_bits, 4) ||
+      misaligned(opts->counters, 8))
+    return fail(LOOPKV_E_INVAL, "decode: q must be 2-byte, out and mask_bits 4-byte, counters 8-byte aligned");
   if (!batch->seq_lens || !batch->block_tables)
     return fail(LOOPKV_E_INVAL, "decode: NULL seq_lens or block_tables");
   if (batch->max_pages < 1) return fail(LOOPKV_E_INVAL, "decode: max_pages must be >= 1");
@@ -537,6 +558,7 @@ int loopkv_vq_append(const loopkv_vq_dims* d, void* pool, int64_t num_pages, con
   if (num_pages < 1) return fail(LOOPKV_E_INVAL, "vq_append: num_pages must be >= 1");
   if (batch->batch < 0 || batch->max_pages < 1 || !batch->seq_lens || !batch->block_tables)
     return fail(LOOPKV_E_INVAL, "vq_append: bad batch");
+  if (const char* be = batch_error(batch)) return fail(LOOPKV_E_INVAL, std::string("vq_append: ") + be);
   if (static_cast<int64_t>(batch->max_pages) * d->page < batch->max_seq_len)
     return fail(LOOPKV_E_INVAL, "vq_append: max_pages * page < max_seq_len");
   if ((reinterpret_cast<uintptr_t>(k_bf16) | reinterpret_cast<uintptr_t>(v_bf16) |
@@ -579,6 +601,9 @@ int loopkv_vq_decode(const loopkv_vq_dims* d, const void* pool, int64_t num_page
   if (num_pages < 1) return fail(LOOPKV_E_INVAL, "vq_decode: num_pages must be >= 1");
   if (batch->batch < 0 || batch->max_pages < 1 || !batch->seq_lens || !batch->block_tables || batch->max_seq_len < 0)
     return fail(LOOPKV_E_INVAL, "vq_decode: bad batch");
+  if (const char* be = batch_error(batch)) return fail(LOOPKV_E_INVAL, std::string("vq_decode: ") + be);
+  if (misaligned(out, 4) || !std::isfinite(sm_scale))
+    return fail(LOOPKV_E_INVAL, "vq_decode: out must be 4-byte aligned and sm_scale finite");
   if (static_cast<int64_t>(batch->max_pages) * d->page < batch->max_seq_len)
     return fail(LOOPKV_E_INVAL, "vq_decode: max_pages * page < max_seq_len");
   if (reinterpret_cast<uintptr_t>(q_bf16) % 8 != 0 ||

@@ -169,6 +169,61 @@ def test_append_and_decode_reject_bad_host_arguments():
     p.close()
 
 
+def test_batch_limits_alignment_and_scale():
+    """Batches above 65535 sequences, misaligned device arrays or outputs and
+    a non-finite sm_scale are rejected before anything is launched (the
+    addresses below are never dereferenced)."""
+    p = abi.Plan(_blob())
+    cells = abi.cell_array(p, {(0, 0): (_FakeTensor(0x1000), _FakeTensor(0x2000), 4, 1),
+                                (1, 0): (_FakeTensor(0x3000), _FakeTensor(0x4000), 4, 1),
+                                (1, 1): (_FakeTensor(0x5000), _FakeTensor(0x6000), 4, 1)})
+    lens, table = _FakeTensor(0x7000, shape=(1,)), _FakeTensor(0x8000, shape=(1, 4))
+    b = abi.make_batch(lens, table, max_seq_len=64)
+    huge = abi.make_batch(lens, table, max_seq_len=64, batch=65536)
+    odd_lens = abi.make_batch(_FakeTensor(0x7002, shape=(1,)), table, max_seq_len=64)
+    odd_table = abi.make_batch(lens, _FakeTensor(0x8001, shape=(1, 4)), max_seq_len=64)
+    lib = abi.lib()
+    k = _FakeTensor(0x9000)
+    ws = _FakeTensor(0xB000, nbytes=1 << 30)
+
+    def app(batch):
+        return lib.loopkv_append(p.handle, ctypes.cast(cells, ctypes.c_void_p), 0, 0, ctypes.byref(batch), 1,
+                                 k.data_ptr(), k.data_ptr(), None)
+
+    def dec(batch=b, q=0x9000, out=0xA000, **kw):
+        opts = abi.make_opts(ws, **kw)
+        return lib.loopkv_decode(p.handle, ctypes.cast(cells, ctypes.c_void_p), 0, 0, ctypes.byref(batch),
+                                 q, out, ctypes.byref(opts), None)
+
+    for call in (app, dec):
+        assert call(huge) == abi.E_INVAL and "65535" in abi.last_error()
+        assert call(odd_lens) == abi.E_INVAL and "4-byte" in abi.last_error()
+        assert call(odd_table) == abi.E_INVAL and "4-byte" in abi.last_error()
+    assert dec(q=0x9001) == abi.E_INVAL and "aligned" in abi.last_error()
+    assert dec(out=0xA002) == abi.E_INVAL and "aligned" in abi.last_error()
+    assert dec(mask_bits=_FakeTensor(0xC002)) == abi.E_INVAL
+    assert dec(counters=_FakeTensor(0xD004)) == abi.E_INVAL
+    assert dec(sm_scale=math.nan) == abi.E_INVAL and "sm_scale" in abi.last_error()
+    assert dec(sm_scale=math.inf) == abi.E_INVAL
+
+    d = abi.vq_dims(4, 2, 128, 32)
+    vws = abi.vq_workspace_bytes(d, 1, 128)
+    vb = abi.make_batch(lens, table, max_seq_len=128)
+    vhuge = abi.make_batch(lens, table, max_seq_len=128, batch=65536)
+
+    def vdec(batch=vb, out=0x9000, scale=1.0):
+        return lib.loopkv_vq_decode(ctypes.byref(d), 0x1000, 4, 0x2000, 0x3000, 0, ctypes.byref(batch), 0x6000,
+                                    out, scale, 0xA000, 1 << 40, None)
+
+    assert vdec(batch=vhuge) == abi.E_INVAL and "65535" in abi.last_error()
+    assert vdec(out=0x9002) == abi.E_INVAL
+    assert vdec(scale=math.nan) == abi.E_INVAL
+    assert lib.loopkv_vq_append(ctypes.byref(d), 0x1000, 4, 0x2000, 0x3000, ctypes.byref(vhuge), 1, 0x4000,
+                                0x5000, None) == abi.E_INVAL
+    assert vws > 0
+    p.close()
+
+
 def _round_up(x, m):
     return (x + m - 1) // m * m
 
