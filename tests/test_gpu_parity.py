@@ -157,6 +157,45 @@ def test_near_uniform_batch_vs_one_split():
         assert rel < 1e-3
 
 
+def test_concurrent_streams_own_workspaces():
+    """Decodes of three cells (every mode) issued on three streams at once,
+    each with its own workspace, output, mask and counters, give the same
+    bits as the same decodes one after another on the default stream."""
+    w = wl.Workload("streams", 230, batch=4, loops=1, layers=3, heads=4, head_dim=128, page=32,
+                    ctx=3000, heavy_frac=0.01)
+    st = runner.CacheState(w, DEV, [[Q4, Q2, Q4]], [[0.01, 0.01, 0.0]])
+    st.prefill()
+    ws_bytes = st.plan.decode_workspace_bytes(w.batch, st.max_seq_len)
+
+    def run(l, stream, ws):
+        q = wl.cell_query(w, st.cell_index(0, l), DEV)[1]
+        out = torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=DEV)
+        mask = st.new_mask()
+        cnt = torch.zeros(2, dtype=torch.int64, device=DEV)
+        opts = abi.make_opts(ws, mask_bits=mask, counters=cnt)
+        if stream is not None:
+            stream.wait_stream(torch.cuda.current_stream())   # inputs were made on the default stream
+        abi.loopkv_decode(st.plan, st.cells, 0, l, st.batch(sum_seq_lens=int(st.lens0.sum())), q, out, opts,
+                          stream=stream)
+        return out, mask, cnt
+
+    ref = {}
+    for l in range(3):
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+        ref[l] = run(l, None, ws)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=DEV) for _ in range(3)]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        got = {l: run(l, streams[l], wss[l]) for l in range(3)}
+        torch.cuda.synchronize()
+        for l in range(3):
+            for a, b in zip(got[l], ref[l]):
+                assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                                   b.view(torch.int32) if b.dtype == torch.float32 else b), (rep, l)
+
+
 @pytest.mark.timeout(300)
 def test_long_sequence_few_pairs():
     """A 600K-token sequence over two (sequence, head) pairs: the automatic
