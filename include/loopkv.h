@@ -87,7 +87,7 @@ const char* loopkv_last_error(void);
  * decides where the low bits are fetched.
  * blob (host, nbytes): "LKVP", u32 version = 1, i32 R, L, H, D, G, P, then
  *   R*L records {u8 kind, u8 pad[3], f32 tau} in [loop][layer] order.
- * Accepted: R >= 1, L >= 1, 1 <= H <= 1024, D in {64, 128}, G == 32,
+ * Accepted: 1 <= R, L <= 4096, 1 <= H <= 1024, D in {64, 128}, G == 32,
  *   P in {16, 32, 64}; kind in {Q4, Q2, REUSE}; REUSE only in loops
  *   0..R-2; tau >= 0 or +inf, never NaN.
  * out: receives a new plan (free with loopkv_plan_free).
@@ -328,6 +328,8 @@ int loopkv_vq_decode(const loopkv_vq_dims* dims, const void* pool, int64_t num_p
  * reused.  Errors: LOOPKV_E_INVAL (bad class or NULL output), LOOPKV_E_HIP.
  */
 enum { LOOPKV_KERNEL_SPLIT = 0, LOOPKV_KERNEL_MERGE = 1, LOOPKV_KERNEL_APPEND = 2 };
+int loopkv_profile_enable(int on);
+int loopkv_profile_collect(int kernel_class, int64_t* launches, double* total_ms);
 
 /*
  * Measurement helper (not an operation of the method): reads `bytes` (a
@@ -338,8 +340,6 @@ enum { LOOPKV_KERNEL_SPLIT = 0, LOOPKV_KERNEL_MERGE = 1, LOOPKV_KERNEL_APPEND = 
  * Errors: LOOPKV_E_INVAL (NULL or unaligned buffer), LOOPKV_E_HIP.
  */
 int loopkv_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
-int loopkv_profile_enable(int on);
-int loopkv_profile_collect(int kernel_class, int64_t* launches, double* total_ms);
 
 #ifdef __cplusplus
 }
