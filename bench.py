@@ -59,8 +59,9 @@ def probe_sizes():
     import torch
     from loop_aware_quantized_amd import abi
     big = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
-    for mb in (256, 512, 805, 1074, 2048, 4096, 8192):
-        n = mb << 20
+    # 50 / 67 MB and 805 / 1074 MB: what one 4K and one 16K decode read (2-bit / 4-bit source)
+    for mb in (50, 67, 256, 512, 805, 1074, 2048, 4096, 8192):
+        n = mb * 10**6 // 4096 * 4096
         reps = max(3, min(50, (8 << 30) // n))
         abi.loopkv_read_probe(big[:n])
         torch.cuda.synchronize()

@@ -237,7 +237,7 @@ int loopkv_profile_enable(int on) {
 int loopkv_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (!buf || bytes < 16 || (reinterpret_cast<uintptr_t>(buf) & 15u))
     return fail(LOOPKV_E_INVAL, "read_probe: buffer must be 16-byte aligned and >= 16 bytes");
-  const hipError_t e = lkv::launch_read_probe(buf, bytes, sink, cu_count() * 16,
+  const hipError_t e = lkv::launch_read_probe(buf, bytes, sink, cu_count() * 12,
                                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail_hip(e, "read_probe: kernel launch");
   g_err.clear();

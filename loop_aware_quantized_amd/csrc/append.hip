@@ -13,6 +13,8 @@
 // is re-quantized over all of them: their raw keys come back from the
 // staging buffer, so the stored cache is a pure function of the token
 // sequence.
+#include <algorithm>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -229,13 +231,15 @@ hipError_t launch_typed(const AppendArgs& a, int batch, hipStream_t stream) {
 
 // Streaming-read probe: each 64-lane workgroup streams one contiguous chunk
 // with four 16-byte loads per lane in flight; the result is written only
-// for an impossible value so the loads stay live.
-constexpr size_t kProbeChunk = 256 << 10;
+// for an impossible value so the loads stay live.  Chunks are multiples of
+// 4 KiB between 16 and 256 KiB, sized so that a launch has about `blocks`
+// workgroups (small buffers still spread over every compute unit).
+constexpr size_t kProbeChunkMin = 16 << 10, kProbeChunkMax = 256 << 10;
 
 __global__ __launch_bounds__(64) void read_probe_kernel(const uint8_t* __restrict__ base, size_t bytes,
-                                                        uint32_t* sink) {
-  const size_t begin = blockIdx.x * kProbeChunk;
-  const size_t end = begin + kProbeChunk < bytes ? begin + kProbeChunk : bytes;
+                                                        size_t chunk, uint32_t* sink) {
+  const size_t begin = blockIdx.x * chunk;
+  const size_t end = begin + chunk < bytes ? begin + chunk : bytes;
   const int lane = threadIdx.x;
   uint32_t acc = 0;
   size_t off = begin;
@@ -252,11 +256,13 @@ __global__ __launch_bounds__(64) void read_probe_kernel(const uint8_t* __restric
 
 }  // namespace
 
-hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int /*blocks*/,
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks,
                              hipStream_t stream) {
-  const size_t chunks = (bytes + kProbeChunk - 1) / kProbeChunk;
+  const size_t want = (bytes + static_cast<size_t>(blocks) - 1) / static_cast<size_t>(blocks);
+  const size_t chunk = std::min(kProbeChunkMax, std::max(kProbeChunkMin, (want + 4095) / 4096 * 4096));
+  const size_t chunks = (bytes + chunk - 1) / chunk;
   hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<unsigned>(chunks)), dim3(64), 0, stream,
-                     static_cast<const uint8_t*>(buf), bytes, sink);
+                     static_cast<const uint8_t*>(buf), bytes, chunk, sink);
   return hipGetLastError();
 }
 
