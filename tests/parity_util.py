@@ -82,7 +82,7 @@ def mask_to_flags(mask_row_words: np.ndarray, T: int) -> np.ndarray:
     return bits.reshape(w.shape[0], -1)[:, :T]
 
 
-def compare_decode(state, r, l, q, out, mask, host_kv, seqs, lens=None):
+def compare_decode(state, r, l, q, out, mask, host_kv, seqs, lens=None, sm_scale=1.0):
     """Compare one decoded cell against the oracle on sequences ``seqs``.
 
     host_kv[b] = (k_bits, v_bits) of the SOURCE cell for sequence b.
@@ -105,7 +105,7 @@ def compare_decode(state, r, l, q, out, mask, host_kv, seqs, lens=None):
         else:
             k_bits, v_bits = host_kv[b]
         cache = _cell_cache(k_bits, v_bits, T, kind)
-        res = oa.decode(cache, q_bits[b], tau)
+        res = oa.decode(cache, q_bits[b], tau, sm_scale=sm_scale)
         if T > 0 and mask_h is not None:
             gflags = mask_to_flags(mask_h[b], T)
             if kind == oc.KIND_Q4:
@@ -119,7 +119,7 @@ def compare_decode(state, r, l, q, out, mask, host_kv, seqs, lens=None):
                 band_total += int(band.sum())
                 flagged += int(res["flags"].sum())
                 flags = np.where(band, gflags, res["flags"])
-                res = oa.decode(cache, q_bits[b], tau, flags=flags)
+                res = oa.decode(cache, q_bits[b], tau, sm_scale=sm_scale, flags=flags)
             else:
                 assert not gflags.any(), "2-bit source must not flag tokens"
         og.append(out_h[b])

@@ -28,14 +28,14 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _decode(st, r, l, num_splits=0, q=None):
+def _decode(st, r, l, num_splits=0, q=None, sm_scale=1.0):
     w = st.w
     if q is None:
         q = wl.cell_query(w, st.cell_index(r, l), DEV)[1]
     out = torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=DEV)
     mask = st.new_mask()
     cnt = torch.zeros(2, dtype=torch.int64, device=DEV)
-    st.decode(r, l, q, out, num_splits=num_splits, mask=mask, counters=cnt)
+    st.decode(r, l, q, out, num_splits=num_splits, mask=mask, counters=cnt, sm_scale=sm_scale)
     torch.cuda.synchronize()
     return q, out, mask, cnt
 
@@ -211,6 +211,66 @@ def test_long_sequence_few_pairs():
     s = compare_decode(st, 0, 0, q, out, mask, kept[(0, 0)], [0, 1])
     say(f"  rel err {s['rel']:.2e} flagged {s['flagged']} band {s['band']}")
     assert s["flagged"] > 1000
+
+
+@pytest.mark.parametrize("sm_scale", [0.0883883, 12.0])
+def test_sm_scale_flat_and_peaky(sm_scale):
+    """Score scales other than 1 in every mode: 1/sqrt(128) (a flat softmax,
+    few tokens reach tau) and 12 (a peaky one, a few tokens hold most of the
+    weight) match the oracle at the same scale, with one split and with the
+    automatic layout."""
+    w = wl.Workload("scale", 210, batch=3, loops=2, layers=3, heads=4, head_dim=128, page=32,
+                    ctx=2500, heavy_frac=0.01)
+    kinds = [[RU, Q2, Q4], [Q4, Q4, Q2]]
+    taus = [[0.002, 0.01, 0.01], [0.0, math.inf, 0.01]]
+    st = runner.CacheState(w, DEV, kinds, taus, lengths=[2500, 777, 64])
+    kept = st.prefill({c: set(range(3)) for c in st.stored})
+    flagged = 0
+    for r in range(2):
+        for l in range(3):
+            src = oa.resolve_source(st.kinds, r, l)
+            for ns in (1, 0):
+                q, out, mask, _ = _decode(st, r, l, num_splits=ns, sm_scale=sm_scale)
+                s = compare_decode(st, r, l, q, out, mask, kept[src], range(3), sm_scale=sm_scale)
+                flagged += s["flagged"]
+                say(f"  scale {sm_scale} cell ({r},{l}) splits {ns}: rel err {s['rel']:.2e} "
+                    f"flagged {s['flagged']} band {s['band']}")
+    if sm_scale > 1.0:
+        assert flagged > 0
+
+
+def test_max_batch_short_sequences():
+    """The largest batch one call takes (65535 sequences, the grids' batch
+    dimension) of 40-token sequences: appends and decodes of a 4-bit sparse
+    and a 2-bit cell match the oracle on sampled sequences, first and last
+    included."""
+    B = 65535
+    w = wl.Workload("maxbatch", 220, batch=B, loops=1, layers=2, heads=2, head_dim=64, page=16,
+                    ctx=40, heavy_frac=0.05)
+    T = 40
+    st = runner.CacheState(w, DEV, [[Q4, Q2]], [[0.05, 0.05]], lengths=[T] * B)
+    seqs = [0, 1, 4097, 32767, B - 2, B - 1]
+    # one bulk draw per cell (the per-sequence draws of the workload
+    # generator would take minutes at this batch)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(220)
+    kept = {}
+    zeros = torch.zeros(B, dtype=torch.int32, device=DEV)
+    for l in range(2):
+        K = torch.randn(B, T, w.heads, w.head_dim, generator=g, device=DEV).to(torch.bfloat16)
+        V = torch.randn(B, T, w.heads, w.head_dim, generator=g, device=DEV).to(torch.bfloat16)
+        batch = abi.make_batch(zeros, st.block_tables, st.max_seq_len)
+        abi.loopkv_append(st.plan, st.cells, 0, l, batch, T, K, V)
+        kept[(0, l)] = {b: (wl.bf16_bits(K[b]), wl.bf16_bits(V[b])) for b in seqs}
+        del K, V
+    torch.cuda.synchronize()
+    for l in range(2):
+        for b in seqs:
+            check_pool(st, 0, l, b, *kept[(0, l)][b])
+        q, out, mask, _ = _decode(st, 0, l)
+        s = compare_decode(st, 0, l, q, out, mask, kept[(0, l)], seqs)
+        say(f"  layer {l}: rel err {s['rel']:.2e} flagged {s['flagged']} band {s['band']}")
+        assert torch.isfinite(out).all()
 
 
 def test_graph_replay_matches_eager():
