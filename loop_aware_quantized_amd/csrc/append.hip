@@ -62,6 +62,19 @@ __global__ __launch_bounds__(kAppendThreads) void append_pack_kernel(AppendArgs 
     return ((static_cast<int64_t>(b) * a.n_new + (t - T0)) * H + h) * D;
   };
 
+  // the new tokens' value tasks (kVT threads per (token, channel group), 4
+  // channels each); the first task's input is requested together with the
+  // keys so that the value pass does not wait for memory again
+  const int first_new = max(gs, T0);
+  const int nv = ge - first_new;
+  const int n_vtasks = nv * kNJ * kVT;
+  auto v_src = [&](int idx) -> const uint2* {
+    const int part = idx % kVT, task = idx / kVT;
+    const int i = task / kNJ, j = task % kNJ;
+    return reinterpret_cast<const uint2*>(a.v_in + new_row(first_new + i) + kGroup * j + 4 * part);
+  };
+  const uint2 v2_first = lane < n_vtasks ? *v_src(lane) : make_uint2(0u, 0u);
+
   // raw keys of the group in 16-byte chunks, staged (old) tokens then new
   // tokens; every load is issued before the first is used
   {
@@ -137,16 +150,14 @@ __global__ __launch_bounds__(kAppendThreads) void append_pack_kernel(AppendArgs 
     if (KIND == kKindQ4) reinterpret_cast<uint32_t*>(blk + L.off_klo + r * L.row)[k] = wlo;
   }
 
-  // value codes and metadata of the new tokens: kVT threads per (token,
-  // channel group), 4 channels each; the group's min and max are combined
-  // over the kVT threads, and each thread writes the byte of its 4 channels
-  const int first_new = max(gs, T0);
-  const int nv = ge - first_new;
-  for (int idx = lane; idx < nv * kNJ * kVT; idx += kAppendThreads) {
+  // value codes and metadata of the new tokens: the group's min and max are
+  // combined over the kVT threads of a task, and each thread writes the byte
+  // of its 4 channels
+  for (int idx = lane; idx < n_vtasks; idx += kAppendThreads) {
     const int part = idx % kVT, task = idx / kVT;
     const int i = task / kNJ, j = task % kNJ;
     const int t = first_new + i;
-    const uint2 v2 = *reinterpret_cast<const uint2*>(a.v_in + new_row(t) + kGroup * j + 4 * part);
+    const uint2 v2 = idx == lane ? v2_first : *v_src(idx);
     const float x[4] = {bf16_to_f32(static_cast<uint16_t>(v2.x & 0xffffu)),
                         bf16_to_f32(static_cast<uint16_t>(v2.x >> 16)),
                         bf16_to_f32(static_cast<uint16_t>(v2.y & 0xffffu)),
