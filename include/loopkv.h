@@ -124,6 +124,19 @@ size_t loopkv_staging_bytes(const loopkv_plan* plan, int loop, int layer,
 size_t loopkv_decode_workspace_bytes(const loopkv_plan* plan, int32_t batch,
                                      int32_t max_seq_len);
 
+/* The split layout loopkv_decode uses for a batch with these host fields
+ * (batch, max_seq_len, sum_seq_lens as in loopkv_batch) and num_splits
+ * (0 = automatic): out[0] = splits per (sequence, head), out[1] = tokens per
+ * split.  Every layout has out[1] a multiple of 64, out[1] <= 4096,
+ * out[1] <= max_seq_len rounded up to 64, out[0] <= 2048 and
+ * out[0] * out[1] >= max_seq_len; the workspace size above holds the
+ * partial records and candidate lists of any such layout.  The automatic
+ * choice depends on the current device's compute-unit count (256 when no
+ * device is visible).  Errors: LOOPKV_E_INVAL (NULL argument, negative
+ * sizes, or a num_splits / max_seq_len that needs more than 2048 splits). */
+int loopkv_decode_splits(const loopkv_plan* plan, int32_t batch, int32_t max_seq_len,
+                         int32_t sum_seq_lens, int32_t num_splits, int32_t out[2]);
+
 /* Memory of one cell; an array of R*L of these is indexed [loop*L + layer].
  * REUSE cells may leave everything NULL / 0. */
 /* Limit: one head's region of a pool, num_pages * head-block bytes, must

@@ -38,6 +38,7 @@ _SIGNATURES = {
     "loopkv_pool_bytes": (c_size_t, [c_void_p, c_int, c_int, c_int64]),
     "loopkv_staging_bytes": (c_size_t, [c_void_p, c_int, c_int, c_int32]),
     "loopkv_decode_workspace_bytes": (c_size_t, [c_void_p, c_int32, c_int32]),
+    "loopkv_decode_splits": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, POINTER(c_int32)]),
     "loopkv_append": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
     "loopkv_decode": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "loopkv_profile_enable": (c_int, [c_int]),
@@ -191,6 +192,13 @@ class Plan:
 
     def decode_workspace_bytes(self, batch: int, max_seq_len: int) -> int:
         return lib().loopkv_decode_workspace_bytes(self.handle, batch, max_seq_len)
+
+    def decode_splits(self, batch: int, max_seq_len: int, sum_seq_lens: int = 0,
+                      num_splits: int = 0) -> tuple[int, int]:
+        """(splits per (sequence, head), tokens per split) of loopkv_decode."""
+        out = (c_int32 * 2)()
+        _check(lib().loopkv_decode_splits(self.handle, batch, max_seq_len, sum_seq_lens, num_splits, out))
+        return int(out[0]), int(out[1])
 
 
 def loopkv_plan_load(blob: bytes) -> Plan:

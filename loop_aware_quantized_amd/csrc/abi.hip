@@ -114,7 +114,8 @@ struct Splits {
 // Automatic splits hold at least 256 tokens (4 tiles), and long sequences
 // over few pairs get longer splits so that no pair has more than
 // kMaxSplits; a requested count gives splits of ceil(t_max / count) tokens
-// rounded up to a tile.  No split exceeds kMaxSplitLen.
+// rounded up to a tile.  No split exceeds kMaxSplitLen or the longest
+// sequence rounded up to a tile.
 Splits choose_splits(int64_t batch, int64_t heads, int t_max, int64_t t_sum, int requested) {
   const int64_t tm = std::max<int64_t>(t_max, 1);
   const int64_t pairs = std::max<int64_t>(batch * heads, 1);
@@ -134,6 +135,10 @@ Splits choose_splits(int64_t batch, int64_t heads, int t_max, int64_t t_sum, int
   len = std::max<int64_t>(len, std::min<int64_t>(256, round_up(tm, lkv::kTile)));
   // long sequences over few pairs: no more than kMaxSplits splits per pair
   len = std::max<int64_t>(len, round_up((tm + lkv::kMaxSplits - 1) / lkv::kMaxSplits, lkv::kTile));
+  // no split longer than the longest sequence (the ragged rule asks for more
+  // when pairs are many and short); the workspace's per-pair candidate
+  // stride relies on it
+  len = std::min<int64_t>(len, round_up(tm, lkv::kTile));
   len = std::min<int64_t>(len, lkv::kMaxSplitLen);
   const int64_t S = (tm + len - 1) / len;
   return {static_cast<int>(S), static_cast<int>(len)};
@@ -364,6 +369,18 @@ size_t loopkv_staging_bytes(const loopkv_plan* plan, int loop, int layer, int32_
 size_t loopkv_decode_workspace_bytes(const loopkv_plan* plan, int32_t batch, int32_t max_seq_len) {
   if (!plan || batch < 0 || max_seq_len < 0) return 0;
   return workspace_plan(batch, plan->H, plan->D, max_seq_len).total;
+}
+
+int loopkv_decode_splits(const loopkv_plan* plan, int32_t batch, int32_t max_seq_len, int32_t sum_seq_lens,
+                         int32_t num_splits, int32_t out[2]) {
+  if (!plan || !out) return fail(LOOPKV_E_INVAL, "decode_splits: NULL plan or out");
+  if (batch < 0 || max_seq_len < 0 || num_splits < 0)
+    return fail(LOOPKV_E_INVAL, "decode_splits: negative batch, max_seq_len or num_splits");
+  const Splits sp = choose_splits(batch, plan->H, max_seq_len, sum_seq_lens > 0 ? sum_seq_lens : 0, num_splits);
+  if (sp.S > lkv::kMaxSplits) return fail(LOOPKV_E_INVAL, "decode_splits: max_seq_len needs too many splits");
+  out[0] = sp.S;
+  out[1] = sp.len;
+  return LOOPKV_OK;
 }
 
 int loopkv_append(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loop, int layer,

@@ -283,3 +283,47 @@ def test_vq_calls_reject_bad_host_arguments():
     assert dec(ws_bytes=ws - 1) == abi.E_CAPACITY and "workspace" in abi.last_error()
     assert dec(batch=big) == abi.E_INVAL
     assert dec(batch=none, ws_bytes=0) == abi.OK               # nothing to decode
+
+
+def _rup(x, m):
+    return (x + m - 1) // m * m
+
+
+@pytest.mark.parametrize("H,D", [(2, 64), (16, 128)])
+def test_decode_splits_fit_the_workspace(H, D):
+    """Every split layout (automatic, for uniform and ragged length hints,
+    or requested) has whole 64-token tiles, at most 4096 tokens per split
+    and no split longer than the longest sequence, covers max_seq_len, and
+    fits the workspace loopkv_decode_workspace_bytes reserves: per (sequence,
+    head) S partial records of D + 4 floats, S candidate counts and S lists
+    of split-length 8-byte entries.  Among the cases: 4096 x 16 short ragged
+    sequences, where the ragged rule alone would ask for splits 4.5x longer
+    than the sequences."""
+    p = abi.Plan(_blob(H=H, D=D, kinds=[[0, 2], [1, 0]]))
+    checked = 0
+    for batch in (1, 7, 64, 512, 4096, 65535):
+        for tm in (0, 1, 63, 64, 128, 1000, 4096, 16384, 100000, 600000, 8388608):
+            for t_sum in (0, batch * tm // 2, batch * tm):
+                for req in (0, 1, 3, 17, 2048):
+                    if t_sum >= 2 ** 31:
+                        continue
+                    try:
+                        S, ln = p.decode_splits(batch, tm, t_sum, req)
+                    except abi.LoopKVError:
+                        # only a requested count can ask for too many splits
+                        assert req > 0 and -(-tm // min(4096, _rup(-(-max(tm, 1) // req), 64))) > 2048
+                        continue
+                    tmax = max(tm, 1)
+                    assert ln % 64 == 0 and 64 <= ln <= 4096 and ln <= _rup(tmax, 64)
+                    assert 1 <= S <= 2048 and S * ln >= tmax and (S - 1) * ln < tmax
+                    if req:   # more than requested only where splits would exceed 4096 tokens
+                        assert S <= max(req, -(-tmax // 4096))
+                    need = batch * H * S * ((D + 4) * 4 + 4 + ln * 8)
+                    assert p.decode_workspace_bytes(batch, tm) >= need, (batch, tm, t_sum, req, S, ln)
+                    checked += 1
+    assert checked > 500
+    # many short ragged pairs: one split per pair, no longer than the longest sequence
+    assert p.decode_splits(4096, 128, 4096 * 80, 0) == (1, 128)
+    with pytest.raises(abi.LoopKVError):
+        p.decode_splits(-1, 128, 0, 0)
+    p.close()

@@ -273,6 +273,48 @@ def test_max_batch_short_sequences():
         assert torch.isfinite(out).all()
 
 
+def test_many_short_ragged_pairs():
+    """4096 sequences x 16 heads of 32-128 tokens with the ragged length hint
+    (the regime where the ragged rule alone asks for splits longer than any
+    sequence): one split per pair, as long as the longest sequence, so the
+    candidate lists stay inside the workspace; sampled sequences of a 4-bit
+    sparse cell (most tokens are candidates at these lengths) and a 2-bit
+    cell match the oracle."""
+    B, T, H, D = 4096, 128, 16, 64
+    w = wl.Workload("manypairs", 230, batch=B, loops=1, layers=2, heads=H, head_dim=D, page=16,
+                    ctx=T, heavy_frac=0.0)
+    st = runner.CacheState(w, DEV, [[Q4, Q2]], [[0.01, 0.01]], lengths=[T] * B)
+    rng = np.random.default_rng(230)
+    # attended lengths are whole key groups, so a prefix of the stored
+    # 128-token sequence is exactly the cache of that prefix
+    lens_np = (32 * rng.integers(1, 5, size=B)).astype(np.int32)
+    lens = torch.from_numpy(lens_np).to(DEV)
+    hint = int(lens_np.sum())
+    assert st.plan.decode_splits(B, T, hint, 0) == (1, T)
+    seqs = sorted({0, 1, 2047, B - 2, B - 1, *rng.choice(B, 5, replace=False).tolist()})
+    g = torch.Generator(device=DEV)
+    g.manual_seed(230)
+    kept = {}
+    zeros = torch.zeros(B, dtype=torch.int32, device=DEV)
+    for l in range(2):
+        K = torch.randn(B, T, H, D, generator=g, device=DEV).to(torch.bfloat16)
+        V = torch.randn(B, T, H, D, generator=g, device=DEV).to(torch.bfloat16)
+        abi.loopkv_append(st.plan, st.cells, 0, l, abi.make_batch(zeros, st.block_tables, st.max_seq_len),
+                          T, K, V)
+        kept[(0, l)] = {b: (wl.bf16_bits(K[b]), wl.bf16_bits(V[b])) for b in seqs}
+        del K, V
+    torch.cuda.synchronize()
+    for l in range(2):
+        q = wl.cell_query(w, st.cell_index(0, l), DEV)[1]
+        out = torch.empty(B, H, D, dtype=torch.float32, device=DEV)
+        mask = st.new_mask()
+        st.decode(0, l, q, out, mask=mask, lens=lens, sum_seq_lens=hint)
+        torch.cuda.synchronize()
+        s = compare_decode(st, 0, l, q, out, mask, kept[(0, l)], seqs, lens=lens_np)
+        say(f"  layer {l}: rel err {s['rel']:.2e} flagged {s['flagged']} band {s['band']}")
+        assert torch.isfinite(out).all()
+
+
 def test_graph_replay_matches_eager():
     """Appends and decodes captured in one HIP graph give, on every replay,
     the same bytes as the same calls made eagerly (eager work and
