@@ -283,7 +283,8 @@ int loopkv_plan_optimize(int32_t R, int32_t L, const double* damage, double dama
  */
 typedef struct {
   int32_t loops;       /* R, 2..4 */
-  int32_t heads;       /* H >= 1 */
+  int32_t heads;       /* H, 1..1024 (the decode grid carries heads in a
+                          dimension of at most 65535 blocks; 1024 as for plans) */
   int32_t head_dim;    /* D, 64 or 128 */
   int32_t page;        /* P, 16, 32 or 64 */
 } loopkv_vq_dims;

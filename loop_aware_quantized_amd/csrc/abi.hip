@@ -521,7 +521,7 @@ namespace {
 const char* vq_dims_error(const loopkv_vq_dims* d) {
   if (!d) return "vq: NULL dims";
   if (d->loops < 2 || d->loops > 4) return "vq: loops must be 2, 3 or 4";
-  if (d->heads < 1) return "vq: heads must be >= 1";
+  if (d->heads < 1 || d->heads > 1024) return "vq: heads must be in [1, 1024]";
   if (d->head_dim != 64 && d->head_dim != 128) return "vq: head_dim must be 64 or 128";
   if (d->page != 16 && d->page != 32 && d->page != 64) return "vq: page must be 16, 32 or 64";
   return nullptr;

@@ -239,7 +239,8 @@ def test_vq_size_queries():
     assert abi.vq_workspace_bytes(d, 3, 0) == _round_up(3 * 16 * 1 * (128 + 4) * 4, 256)
     d64 = abi.vq_dims(2, 2, 64, 16)
     assert abi.vq_codebook_bytes(d64) == 2 * 256 * 16 * 4 * 2
-    for bad in [(1, 16, 128, 32), (5, 16, 128, 32), (4, 0, 128, 32), (4, 16, 96, 32), (4, 16, 128, 8)]:
+    for bad in [(1, 16, 128, 32), (5, 16, 128, 32), (4, 0, 128, 32), (4, 1025, 128, 32), (4, 16, 96, 32),
+                (4, 16, 128, 8)]:
         bd = abi.vq_dims(*bad)
         assert abi.vq_codebook_bytes(bd) == 0
         assert abi.vq_pool_bytes(bd, 4) == 0
