@@ -253,7 +253,8 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells,
  * The search is exact (dynamic program over layers; O(L * (20R L)^2 / 3)
  *   time for R = 4).
  * Errors: LOOPKV_E_INVAL (R not in 1..8, L not in 1..4096, NULL pointers,
- *   negative / non-finite inputs, instance too large), LOOPKV_E_PLAN (no
+ *   negative / non-finite inputs, instance too large, host memory for the
+ *   search tables not available), LOOPKV_E_PLAN (no
  *   plan meets both budgets).
  */
 int loopkv_plan_optimize(int32_t R, int32_t L, const double* damage, double damage_budget,

@@ -18,6 +18,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <new>
 #include <vector>
 
 #include "loopkv.h"
@@ -48,8 +49,8 @@ int fail(int code, const char* msg) {
 
 }  // namespace
 
-extern "C" int loopkv_plan_optimize(int32_t R, int32_t L, const double* damage, double damage_budget,
-                                    int64_t storage_budget, uint8_t* kinds, double* totals) {
+static int plan_optimize(int32_t R, int32_t L, const double* damage, double damage_budget,
+                         int64_t storage_budget, uint8_t* kinds, double* totals) {
   if (R < 1 || R > 8 || L < 1 || L > 4096) return fail(LOOPKV_E_INVAL, "plan_optimize: need 1 <= R <= 8, 1 <= L <= 4096");
   if (!damage || !kinds) return fail(LOOPKV_E_INVAL, "plan_optimize: NULL damage or kinds");
   if (!(damage_budget >= 0.0) || storage_budget < 0)
@@ -173,4 +174,15 @@ extern "C" int loopkv_plan_optimize(int32_t R, int32_t L, const double* damage, 
     totals[2] = best_d;
   }
   return LOOPKV_OK;
+}
+
+// The search tables can take up to about 0.5 GiB of host memory: an
+// allocation failure is reported as an error, not thrown across the ABI.
+extern "C" int loopkv_plan_optimize(int32_t R, int32_t L, const double* damage, double damage_budget,
+                                    int64_t storage_budget, uint8_t* kinds, double* totals) {
+  try {
+    return plan_optimize(R, L, damage, damage_budget, storage_budget, kinds, totals);
+  } catch (const std::bad_alloc&) {
+    return fail(LOOPKV_E_INVAL, "plan_optimize: out of host memory for the search tables");
+  }
 }
