@@ -302,8 +302,13 @@ int loopkv_plan_load(const void* blob, size_t nbytes, loopkv_plan** out) {
   loopkv_plan* plan = new (std::nothrow) loopkv_plan;
   if (!plan) return fail(LOOPKV_E_PLAN, "plan_load: out of host memory");
   plan->R = R; plan->L = L; plan->H = H; plan->D = D; plan->G = G; plan->P = P;
-  plan->kind.resize(cells);
-  plan->tau.resize(cells);
+  try {
+    plan->kind.resize(cells);
+    plan->tau.resize(cells);
+  } catch (const std::bad_alloc&) {
+    delete plan;
+    return fail(LOOPKV_E_PLAN, "plan_load: out of host memory");
+  }
   for (size_t c = 0; c < cells; ++c) {
     const uint8_t* rec = p + 32 + 8 * c;
     const int loop = static_cast<int>(c / L), layer = static_cast<int>(c % L);
