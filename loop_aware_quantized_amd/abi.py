@@ -123,9 +123,13 @@ def _check(rc: int) -> int:
 
 
 def _ptr(t) -> int | None:
-    """Device (or host) address of a torch tensor, None for None."""
+    """Address of a device tensor, None for None.  Every buffer the library
+    takes is device memory, so a host torch tensor is refused here rather
+    than handed to a kernel."""
     if t is None:
         return None
+    if not getattr(t, "is_cuda", True):
+        raise ValueError(f"loopkv: expected a device tensor, got one on {t.device}")
     return t.data_ptr()
 
 

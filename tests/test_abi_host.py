@@ -328,3 +328,11 @@ def test_decode_splits_fit_the_workspace(H, D):
     with pytest.raises(abi.LoopKVError):
         p.decode_splits(-1, 128, 0, 0)
     p.close()
+
+
+def test_binding_refuses_host_tensors():
+    """The binding passes device addresses only: a host torch tensor is
+    refused before any call into the library."""
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError, match="device tensor"):
+        abi.make_batch(torch.zeros(1, dtype=torch.int32), torch.zeros(1, 4, dtype=torch.int32), max_seq_len=64)
