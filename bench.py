@@ -122,7 +122,9 @@ class Bench:
         self.kinds, self.taus = kinds, taus
         dev = torch.device("cuda", 0)
         self.dev = dev
-        self.steps_per_point = args.warmup + args.steps + 2   # + per-kernel pass + counters pass
+        # warmup + timed steps + the same steps unprofiled (or, with --graph, an
+        # eager profiled pass) + a counters step
+        self.steps_per_point = args.warmup + 2 * args.steps + 2
         extra = w.append_tokens * self.steps_per_point * n_points
         t0 = time.time()
         st = runner.CacheState(w, dev, kinds, taus, extra_tokens=extra)
@@ -219,35 +221,52 @@ class Bench:
             tot += tok * H * per
         return tot
 
+    def timed_steps(self, n, hook):
+        """n steps between events on the launch stream; with hook, the library
+        stamps every kernel's own start and end (hipExtLaunchKernel events).
+        Returns (first step index, events, per-class (launches, ms))."""
+        torch, abi = self.torch, self.abi
+        classes = (("split", abi.KERNEL_SPLIT), ("merge", abi.KERNEL_MERGE), ("append", abi.KERNEL_APPEND))
+        if hook:
+            abi.loopkv_profile_enable(True)
+            for _, c in classes:
+                abi.loopkv_profile_collect(c)
+        first = self.step_idx
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        evs[0].record()
+        for i in range(n):
+            self.step(eager=hook)
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        kst = None
+        if hook:
+            kst = {name: abi.loopkv_profile_collect(c) for name, c in classes}
+            abi.loopkv_profile_enable(False)
+        return first, evs, kst
+
     def run_point(self):
-        """Warmup, timed steps, a per-kernel pass and a counters pass."""
+        """Warmup, timed steps (kernel durations stamped live), the same number
+        of steps unprofiled, and a counters step."""
         torch, abi, args, w = self.torch, self.abi, self.args, self.w
         self.graph = None
         for _ in range(args.warmup):
             self.step()
         torch.cuda.synchronize()
         if args.graph:
+            # a captured step is replayed unprofiled; kernel durations come
+            # from an eager profiled pass of the same length
             self.capture()
-        first = self.step_idx
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-        evs[0].record()
-        for i in range(args.steps):
-            self.step()
-            evs[i + 1].record()
-        torch.cuda.synchronize()
+            first, evs, _ = self.timed_steps(args.steps, hook=False)
+            prof_first, _, kst = self.timed_steps(args.steps, hook=True)
+            other_ms = None
+        else:
+            first, evs, kst = self.timed_steps(args.steps, hook=True)
+            prof_first = first
+            _, evs2, _ = self.timed_steps(args.steps, hook=False)
+            other_ms = evs2[0].elapsed_time(evs2[-1]) / args.steps
         total_ms = evs[0].elapsed_time(evs[-1])
         ms_per_step = total_ms / args.steps
         self.step_spread = step_spread(evs)
-        # per-kernel durations: library events around every launch of one step
-        abi.loopkv_profile_enable(True)
-        for c in (abi.KERNEL_SPLIT, abi.KERNEL_MERGE, abi.KERNEL_APPEND):
-            abi.loopkv_profile_collect(c)
-        prof_step = self.step_idx
-        self.step(eager=True)
-        torch.cuda.synchronize()
-        kst = {name: abi.loopkv_profile_collect(c) for name, c in
-               (("split", abi.KERNEL_SPLIT), ("merge", abi.KERNEL_MERGE), ("append", abi.KERNEL_APPEND))}
-        abi.loopkv_profile_enable(False)
         # low-plane rows actually fetched (library counters)
         cnt = torch.zeros(2, dtype=torch.int64, device=self.dev)
         cnt_step = self.step_idx
@@ -269,7 +288,7 @@ class Bench:
         step_bytes = self.split_bytes(lens_t) + (lo_bytes - dense_lo) + fixed
         step_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
         n_split, split_ms = kst["split"]
-        split_alg = self.split_bytes(self.lens_of(prof_step))
+        split_alg = sum(self.split_bytes(self.lens_of(s)) for s in range(prof_first, prof_first + args.steps))
         achieved = split_alg / (split_ms / 1e3) / 1e9 if split_ms > 0 else 0.0
         lo_stored = sum(int(self.lens_of(cnt_step).sum()) * H * D // 4
                         for (r, l) in self.order if self.src_kind(r, l) == self.wl.KIND_Q4)
@@ -277,7 +296,8 @@ class Bench:
             "value": value, "ms_per_step": ms_per_step, "step_ms": self.step_spread,
             "hbm_gbs_required": step_gbs, "bytes_required_per_step": step_bytes,
             "split": {"launches": n_split, "ms": split_ms, "alg_bytes": split_alg, "achieved_gbs": achieved},
-            "kernels_ms_per_step": {k: v[1] for k, v in kst.items()},
+            "kernels_ms_per_step": {k: v[1] / args.steps for k, v in kst.items()},
+            "ms_per_step_unprofiled": other_ms,
             "lo_plane": {"flagged_token_heads": flagged, "lo_bytes_read": lo_bytes,
                          "lo_bytes_stored_4bit_sources": lo_stored,
                          "fraction_read": lo_bytes / lo_stored if lo_stored else None},
@@ -606,6 +626,7 @@ def main():
                      "frac_of_measured_read_peak": sp["achieved_gbs"] / peak},
         "kernels_ms_per_step": primary["kernels_ms_per_step"],
         "step_ms": primary["step_ms"],
+        "ms_per_step_unprofiled": primary["ms_per_step_unprofiled"],
         "lo_plane": primary["lo_plane"],
         "storage": {"stored_bytes": stored_bytes, "all_4bit_bytes": all_q4_bytes,
                     "saving_vs_all_4bit": (1 - stored_bytes / all_q4_bytes) if all_q4_bytes else None},

@@ -335,7 +335,11 @@ int loopkv_vq_decode(const loopkv_vq_dims* dims, const void* pool, int64_t num_p
 /*
  * Measurement hook (not an operation of the method; used by benchmarks to
  * time kernels live).  While enabled, every kernel launch this library makes
- * is bracketed by a pair of HIP events recorded on the launch's own stream.
+ * carries a pair of HIP events that the runtime stamps with that kernel's
+ * own start and end on the launch's stream (hipExtLaunchKernel); nothing is
+ * recorded between launches, so kernels run back to back as they do
+ * unprofiled.  An append's interval runs from its first kernel's start to
+ * its last kernel's end.
  * loopkv_profile_collect waits for the recorded events of one kernel class
  * (LOOPKV_KERNEL_*), returns the number of launches and their summed
  * duration in milliseconds, and clears that class.  Enabling/disabling is

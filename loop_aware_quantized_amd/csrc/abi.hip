@@ -191,10 +191,10 @@ int debug_check(const loopkv_batch* bt, int P, int64_t num_pages, int extra, int
   return LOOPKV_OK;
 }
 
-// ---- measurement hook: event pairs around launches, per kernel class ----
+// ---- measurement hook: kernel-stamped event pairs, per kernel class -----
 struct ProfClass {
   std::vector<hipEvent_t> ev;  // start, stop, start, stop, ...
-  size_t used = 0;             // events recorded since the last collect
+  size_t used = 0;             // events handed out since the last collect
 };
 
 struct Profiler {
@@ -212,20 +212,21 @@ Profiler& profiler() {
 
 namespace lkv {
 
-void prof_mark(int c, int phase, hipStream_t stream) {
+ProfEvents prof_events(int c) {
   Profiler& p = profiler();
   std::lock_guard<std::mutex> lock(p.mu);
-  if (!p.on) return;
+  ProfEvents out;
+  if (!p.on) return out;
   ProfClass& pc = p.cls[c];
-  // a stop mark pairs with the start recorded just before it
-  if (phase == 1 && pc.used % 2 == 0) return;
-  if (phase == 0 && pc.used % 2 == 1) pc.used -= 1;  // unmatched start: reuse its slot
-  if (pc.used == pc.ev.size()) {
+  while (pc.ev.size() < pc.used + 2) {
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return;
+    if (hipEventCreate(&e) != hipSuccess) return out;
     pc.ev.push_back(e);
   }
-  if (hipEventRecord(pc.ev[pc.used], stream) == hipSuccess) pc.used += 1;
+  out.start = pc.ev[pc.used];
+  out.stop = pc.ev[pc.used + 1];
+  pc.used += 2;
+  return out;
 }
 
 }  // namespace lkv

@@ -229,14 +229,17 @@ __global__ __launch_bounds__(64) void append_staging_kernel(AppendArgs a) {
 template <int D, int KIND>
 hipError_t launch_typed(const AppendArgs& a, int batch, hipStream_t stream) {
   const int groups = (a.n_new + kGroup - 1) / kGroup + 1;
-  prof_mark(kClassAppend, 0, stream);
-  hipLaunchKernelGGL((append_pack_kernel<D, KIND>), dim3(groups, a.H, batch), dim3(kAppendThreads), 0, stream, a);
+  // one timed interval from the pack kernel's start to the last kernel's end
+  const ProfEvents ev = prof_events(kClassAppend);
+  const bool staging = a.n_new > 1;
+  hipExtLaunchKernelGGL((append_pack_kernel<D, KIND>), dim3(groups, a.H, batch), dim3(kAppendThreads), 0, stream,
+                        ev.start, staging ? nullptr : ev.stop, 0, a);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && a.n_new > 1) {
-    hipLaunchKernelGGL((append_staging_kernel<D>), dim3(a.H, batch), dim3(64), 0, stream, a);
+  if (e == hipSuccess && staging) {
+    hipExtLaunchKernelGGL((append_staging_kernel<D>), dim3(a.H, batch), dim3(64), 0, stream, nullptr, ev.stop,
+                          0, a);
     e = hipGetLastError();
   }
-  prof_mark(kClassAppend, 1, stream);
   return e;
 }
 
@@ -254,12 +257,19 @@ __global__ __launch_bounds__(64) void read_probe_kernel(const uint8_t* __restric
   const int lane = threadIdx.x;
   uint32_t acc = 0;
   size_t off = begin;
+  // buffer loads over the chunk with the non-temporal hint (cache-policy
+  // bit 1), as the decode kernels stream the cache
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(base + begin), static_cast<short>(0), static_cast<int>(end - begin), 0x00020000);
+  const uint32_t lo = static_cast<uint32_t>(lane * 16);
   for (; off + 4096 <= end; off += 4096) {
-    const uint4 a = *reinterpret_cast<const uint4*>(base + off + lane * 16);
-    const uint4 b = *reinterpret_cast<const uint4*>(base + off + 1024 + lane * 16);
-    const uint4 c = *reinterpret_cast<const uint4*>(base + off + 2048 + lane * 16);
-    const uint4 d = *reinterpret_cast<const uint4*>(base + off + 3072 + lane * 16);
-    acc ^= a.x ^ b.y ^ c.z ^ d.w;
+    const uint32_t o = static_cast<uint32_t>(off - begin);
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(rsrc, lo, o, 2);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b128(rsrc, lo, o + 1024, 2);
+    const auto c = __builtin_amdgcn_raw_buffer_load_b128(rsrc, lo, o + 2048, 2);
+    const auto d = __builtin_amdgcn_raw_buffer_load_b128(rsrc, lo, o + 3072, 2);
+    acc ^= (a[0] ^ a[1] ^ a[2] ^ a[3]) ^ (b[0] ^ b[1] ^ b[2] ^ b[3]) ^ (c[0] ^ c[1] ^ c[2] ^ c[3]) ^
+           (d[0] ^ d[1] ^ d[2] ^ d[3]);
   }
   for (off += lane * 16; off + 16 <= end; off += 1024) acc ^= reinterpret_cast<const uint4*>(base + off)->x;
   if (acc == 0x9E3779B9u && sink) sink[0] = acc;

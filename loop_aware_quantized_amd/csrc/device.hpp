@@ -124,6 +124,41 @@ __device__ __forceinline__ float dpp_wave_max(float v) {
   return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
+// wave-uniform maximum of an unsigned value (DPP row max + four lanes)
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t dpp_wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0xB1>(v));
+  v = max(v, dpp_u<0x4E>(v));
+  v = max(v, dpp_u<0x141>(v));
+  v = max(v, dpp_u<0x140>(v));
+  const uint32_t a = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0));
+  const uint32_t b = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16));
+  const uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32));
+  const uint32_t d = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+  return max(max(a, b), max(c, d));
+}
+
+// Wave-uniform maximum of a float that is not NaN, as an integer maximum:
+// flipping the magnitude bits of negative values makes the signed integer
+// order the float order, and DPP integer maxima need no NaN canonicalizing.
+__device__ __forceinline__ int f32_order_key(float x) {
+  const int i = __float_as_int(x);
+  return i ^ ((i >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float dpp_wave_max_ordered(float x) {
+  int v = f32_order_key(x);
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));
+  const int m = max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+                    max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  return __int_as_float(m ^ ((m >> 31) & 0x7fffffff));   // the key map is its own inverse
+}
+
 __device__ __forceinline__ float byte_f(uint32_t w, int k) {
   return static_cast<float>((w >> (8 * k)) & 0xffu);
 }

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <cstdint>
 
 #include "layout.hpp"
@@ -54,10 +55,16 @@ enum DecodeMode : int {
   kModeDense = 2,      // 4-bit, tau = 0: every low plane read in the split pass
 };
 
-// Measurement hook: brackets one launch of kernel class `cls` with events
-// when profiling is enabled (no-op otherwise).  phase 0 = before, 1 = after.
+// Measurement hook.  While profiling is enabled, prof_events(cls) hands out
+// a fresh event pair for one launch of kernel class `cls`; the launch passes
+// it to hipExtLaunchKernel, which stamps the kernel's own start and end on
+// the launch stream (nothing is recorded between launches, so the timed
+// kernels run back to back as they do unprofiled).  Otherwise both are null.
 enum { kClassSplit = 0, kClassMerge = 1, kClassAppend = 2, kClasses = 3 };
-void prof_mark(int cls, int phase, hipStream_t stream);
+struct ProfEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfEvents prof_events(int cls);
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t stream);
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks,

@@ -405,24 +405,24 @@ __global__ __launch_bounds__(kSplitThreads) void vq_split_kernel(VqArgs a) {
 template <int D, int R>
 hipError_t launch_encode_t(const VqArgs& a, hipStream_t stream) {
   const int64_t M = static_cast<int64_t>(a.batch) * a.n_new * a.H;
+  const ProfEvents ev = prof_events(kClassAppend);
   if (M <= 16384) {                        // few token-heads (a decode step): four threads each
     constexpr int kPer = kThreads / 4;
     const dim3 grid(static_cast<unsigned>((M + kPer - 1) / kPer), D / kVqSub, 2);
-    hipLaunchKernelGGL((vq_encode_kernel<D, R, 4>), grid, dim3(kThreads), 0, stream, a);
+    hipExtLaunchKernelGGL((vq_encode_kernel<D, R, 4>), grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a);
   } else {
     const dim3 grid(static_cast<unsigned>((M + kThreads - 1) / kThreads), D / kVqSub, 2);
-    hipLaunchKernelGGL((vq_encode_kernel<D, R, 1>), grid, dim3(kThreads), 0, stream, a);
+    hipExtLaunchKernelGGL((vq_encode_kernel<D, R, 1>), grid, dim3(kThreads), 0, stream, ev.start, ev.stop, 0, a);
   }
   return hipGetLastError();
 }
 
 template <int D, int R>
 hipError_t launch_split_t(const VqArgs& a, hipStream_t stream) {
-  prof_mark(kClassSplit, 0, stream);
-  hipLaunchKernelGGL((vq_split_kernel<D, R>), dim3(a.S, a.H, a.batch), dim3(kSplitThreads), 0, stream, a);
-  const hipError_t e = hipGetLastError();
-  prof_mark(kClassSplit, 1, stream);
-  return e;
+  const ProfEvents ev = prof_events(kClassSplit);
+  hipExtLaunchKernelGGL((vq_split_kernel<D, R>), dim3(a.S, a.H, a.batch), dim3(kSplitThreads), 0, stream,
+                        ev.start, ev.stop, 0, a);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -446,10 +446,7 @@ hipError_t launch_split_d(const VqArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_vq_encode(const VqArgs& a, int D, hipStream_t stream) {
-  prof_mark(kClassAppend, 0, stream);
-  const hipError_t e = D == 128 ? launch_encode_d<128>(a, stream) : launch_encode_d<64>(a, stream);
-  prof_mark(kClassAppend, 1, stream);
-  return e;
+  return D == 128 ? launch_encode_d<128>(a, stream) : launch_encode_d<64>(a, stream);
 }
 
 hipError_t launch_vq_split(const VqArgs& a, int D, hipStream_t stream) {

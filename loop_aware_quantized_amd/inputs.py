@@ -46,6 +46,7 @@ class Workload:
     taus: tuple = (0.01,)         # "random": per-cell draw; else one tau for all cells
     append_tokens: int = 0        # tokens appended per stored cell in one step
     tau_sweep: tuple = field(default=())
+    value_scale: float = 1.0      # prefill values are N(0, value_scale^2)
 
     @property
     def cells(self) -> int:
@@ -275,7 +276,7 @@ def cell_kv(w: Workload, cell: int, tokens: int, device, b0: int = 0, b1: int | 
             heavy = torch.rand(tokens, H, generator=g, device=device) < w.heavy_frac
         K = torch.where(heavy[..., None], 0.5 * qraw[b][None] + K, K)
         K = K * mult[None]
-        V = torch.randn(tokens, H, D, generator=g, device=device)
+        V = torch.randn(tokens, H, D, generator=g, device=device) * w.value_scale
         ks.append(K.to(torch.bfloat16))
         vs.append(V.to(torch.bfloat16))
     return torch.stack(ks), torch.stack(vs)

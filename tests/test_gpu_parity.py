@@ -138,6 +138,29 @@ def test_small_tau_candidate_spill(tau):
             assert s["flagged"] > 0
 
 
+@pytest.mark.parametrize("vscale", [1.0, 1e-2, 1e-4, 1e-5])
+def test_small_value_magnitudes(vscale):
+    """Values of magnitude 1 down to 1e-5 (value scales deep in fp16's
+    subnormal range): 4-bit sparse, plain and dense cells and a 2-bit cell,
+    with one split and the automatic layout, stay within the 2e-3 bound.
+    The split pass's fp16 value weights p * s would lose it below 1e-4
+    without the weight exponent it carries."""
+    w = wl.Workload(f"vscale-{vscale:g}", 240, batch=3, loops=1, layers=4, heads=4, head_dim=128, page=32,
+                    ctx=3000, heavy_frac=0.01, value_scale=vscale)
+    st = runner.CacheState(w, DEV, [[Q4, Q4, Q4, Q2]], [[0.01, math.inf, 0.0, 0.01]],
+                           lengths=[3000, 1777, 64])
+    kept = st.prefill({c: set(range(3)) for c in st.stored})
+    worst = 0.0
+    for l in range(4):
+        for ns in (1, 0):
+            q, out, mask, _ = _decode(st, 0, l, num_splits=ns)
+            s = compare_decode(st, 0, l, q, out, mask, kept[(0, l)], range(3))
+            worst = max(worst, s["rel"])
+            say(f"  vscale {vscale:g} layer {l} splits {ns}: rel err {s['rel']:.2e} |o| {s['scale']:.2e} "
+                f"flagged {s['flagged']} band {s['band']}")
+    assert worst < 1e-3
+
+
 def test_near_uniform_batch_vs_one_split():
     """16 x 16 (sequence, head) pairs of near-equal length in the automatic
     split layout: every mode matches the oracle, and the outputs match the
