@@ -231,6 +231,31 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells,
                   const loopkv_decode_opts* opts, void* stream);
 
 /*
+ * loopkv_decode_noalloc -- loopkv_decode for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results as
+ * loopkv_decode (bit for bit), except that opts->workspace and
+ * opts->workspace_bytes are ignored: the split partials, candidate counts
+ * and candidate lists live in a device array the library holds, one copy of
+ * LOOPKV_NOALLOC_SCRATCH_BYTES per GPU it runs on, until the process ends.
+ * The call allocates nothing.  loopkv_decode_noalloc_bytes gives the bytes
+ * a call with these host fields would use (0 for invalid arguments); a
+ * batch that needs more fails with LOOPKV_E_CAPACITY before any launch.
+ * No initial contents are needed.  Every call on one GPU uses that GPU's
+ * copy: calls that overlap on one GPU (on different streams, or from host
+ * threads without stream ordering) race and give undefined results.
+ * Errors: as loopkv_decode; LOOPKV_E_CAPACITY when the batch needs more
+ *   than LOOPKV_NOALLOC_SCRATCH_BYTES.
+ */
+#define LOOPKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+size_t loopkv_decode_noalloc_bytes(const loopkv_plan* plan, int loop, int layer, int32_t batch,
+                                   int32_t max_seq_len, int32_t sum_seq_lens, int32_t num_splits);
+int loopkv_decode_noalloc(const loopkv_plan* plan, const loopkv_cell_mem* cells,
+                          int loop, int layer, const loopkv_batch* batch,
+                          const void* q_bf16, float* out,
+                          const loopkv_decode_opts* opts, void* stream);
+
+/*
  * loopkv_plan_optimize -- offline plan search: the kind of every cell that
  * minimizes decode reads under a damage budget and a storage budget.
  * Source: LoopKV abstract -- the model's output damage is close to the sum

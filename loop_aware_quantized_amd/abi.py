@@ -41,6 +41,9 @@ _SIGNATURES = {
     "loopkv_decode_splits": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, POINTER(c_int32)]),
     "loopkv_append": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
     "loopkv_decode": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "loopkv_decode_noalloc_bytes": (c_size_t, [c_void_p, c_int, c_int, c_int32, c_int32, c_int32, c_int32]),
+    "loopkv_decode_noalloc": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p]),
     "loopkv_profile_enable": (c_int, [c_int]),
     "loopkv_profile_collect": (c_int, [c_int, POINTER(c_int64), POINTER(ctypes.c_double)]),
     "loopkv_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
@@ -261,6 +264,24 @@ def loopkv_decode(plan: Plan, cells, loop: int, layer: int, batch: Batch, q, out
     return _check(lib().loopkv_decode(plan.handle, ctypes.cast(cells, c_void_p), loop, layer,
                                       ctypes.byref(batch), _ptr(q), _ptr(out), ctypes.byref(opts),
                                       _stream_handle(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def loopkv_decode_noalloc(plan: Plan, cells, loop: int, layer: int, batch: Batch, q, out,
+                          opts: DecodeOpts, stream=None) -> int:
+    """loopkv_decode on the library's fixed device scratch (opts' workspace ignored)."""
+    return _check(lib().loopkv_decode_noalloc(plan.handle, ctypes.cast(cells, c_void_p), loop, layer,
+                                              ctypes.byref(batch), _ptr(q), _ptr(out), ctypes.byref(opts),
+                                              _stream_handle(stream)))
+
+
+def loopkv_decode_noalloc_bytes(plan: Plan, loop: int, layer: int, batch: int, max_seq_len: int,
+                                sum_seq_lens: int = 0, num_splits: int = 0) -> int:
+    """Scratch bytes loopkv_decode_noalloc would use (0 for invalid arguments)."""
+    return lib().loopkv_decode_noalloc_bytes(plan.handle, loop, layer, batch, max_seq_len, sum_seq_lens,
+                                             num_splits)
 
 
 def loopkv_profile_enable(on: bool) -> int:

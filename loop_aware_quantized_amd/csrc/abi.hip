@@ -444,55 +444,135 @@ int loopkv_append(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
   return LOOPKV_OK;
 }
 
-int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loop, int layer,
-                  const loopkv_batch* batch, const void* q_bf16, float* out,
-                  const loopkv_decode_opts* opts, void* stream) {
-  if (!plan || !cells || !batch || !opts) return fail(LOOPKV_E_INVAL, "decode: NULL plan, cells, batch or opts");
-  if (!cell_ok(plan, loop, layer)) return fail(LOOPKV_E_INVAL, "decode: no such cell");
+}  // extern "C"
+
+// ---- decode: shared by the workspace and the allocation-free entry points --
+
+namespace {
+
+// File-scope scratch of the allocation-free decode: one copy per GPU, held
+// until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host it is only a stand-in for the symbol); it uses the
+// device address looked up once per device by static_scratch_ptr().
+constexpr size_t kStaticScratchBytes = LOOPKV_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+// Device address of `scratch` on the current device (NULL on failure, with
+// the HIP error in *err).  Looked up with that device current on its first
+// use and kept per device.
+uint8_t* static_scratch_ptr(hipError_t* err) {
+  static std::mutex mu;
+  static std::vector<uint8_t*> by_device;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= static_cast<int>(by_device.size())) by_device.resize(dev + 1, nullptr);
+  if (!by_device[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    by_device[dev] = static_cast<uint8_t*>(ptr);
+  }
+  *err = hipSuccess;
+  return by_device[dev];
+}
+
+// Scratch an allocation-free decode of this batch uses: partial records and
+// candidate counts for the chosen split layout, and candidate lists (one
+// entry per token of a split) only when a tau mask is formed.
+struct CompactScratch {
+  size_t partials, counts, cand, total;
+};
+
+CompactScratch compact_scratch(int64_t batch, int64_t H, int64_t D, const Splits& sp, bool sparse) {
+  const int64_t recs = batch * H * sp.S;
+  CompactScratch c;
+  c.partials = static_cast<size_t>(round_up(recs * (D + lkv::kPartialPad) * 4, 256));
+  c.counts = static_cast<size_t>(round_up(recs * 4, 256));
+  c.cand = sparse ? static_cast<size_t>(round_up(recs * sp.len * 8, 256)) : 0;
+  c.total = c.partials + c.counts + c.cand;
+  return c;
+}
+
+int decode_mode(int src_kind, float tau) {
+  if (src_kind != lkv::kKindQ4) return lkv::kModePlain;
+  if (tau == 0.0f) return lkv::kModeDense;
+  return std::isfinite(tau) ? lkv::kModeSparse : lkv::kModePlain;
+}
+
+// Everything loopkv_decode checks and launches.  static_scratch: take the
+// partials and candidate lists from the file-scope scratch (sized by the
+// actual split layout) instead of opts->workspace.
+int decode_impl(const char* who, const loopkv_plan* plan, const loopkv_cell_mem* cells, int loop, int layer,
+                const loopkv_batch* batch, const void* q_bf16, float* out, const loopkv_decode_opts* opts,
+                void* stream, bool static_scratch) {
+  const std::string w(who);
+  if (!plan || !cells || !batch || !opts) return fail(LOOPKV_E_INVAL, w + ": NULL plan, cells, batch or opts");
+  if (!cell_ok(plan, loop, layer)) return fail(LOOPKV_E_INVAL, w + ": no such cell");
   const size_t c = static_cast<size_t>(loop) * plan->L + layer;
   const int src_loop = plan->kind[c] == lkv::kKindReuse ? plan->R - 1 : loop;
   const size_t sc = static_cast<size_t>(src_loop) * plan->L + layer;
   const int src_kind = plan->kind[sc];
   const float tau = plan->tau[c];
   const loopkv_cell_mem& mem = cells[sc];
-  if (!mem.pool) return fail(LOOPKV_E_INVAL, "decode: source cell pool is NULL");
-  if (mem.num_pages < 1) return fail(LOOPKV_E_INVAL, "decode: source cell has no pages");
+  if (!mem.pool) return fail(LOOPKV_E_INVAL, w + ": source cell pool is NULL");
+  if (mem.num_pages < 1) return fail(LOOPKV_E_INVAL, w + ": source cell has no pages");
   if (static_cast<uint64_t>(mem.num_pages) * lkv::make_layout(src_kind, plan->P, plan->D).HB > 0xFFFFFFFFull)
-    return fail(LOOPKV_E_INVAL, "decode: one head's pool region (num_pages * head-block bytes) exceeds 4 GiB");
-  if (batch->batch < 0) return fail(LOOPKV_E_INVAL, "decode: negative batch");
-  if (const char* be = batch_error(batch)) return fail(LOOPKV_E_INVAL, std::string("decode: ") + be);
-  if (opts->num_splits < 0) return fail(LOOPKV_E_INVAL, "decode: num_splits must be >= 0");
-  if (batch->max_seq_len < 0) return fail(LOOPKV_E_INVAL, "decode: negative max_seq_len");
-  if (!std::isfinite(opts->sm_scale)) return fail(LOOPKV_E_INVAL, "decode: sm_scale must be finite");
+    return fail(LOOPKV_E_INVAL, w + ": one head's pool region (num_pages * head-block bytes) exceeds 4 GiB");
+  if (batch->batch < 0) return fail(LOOPKV_E_INVAL, w + ": negative batch");
+  if (const char* be = batch_error(batch)) return fail(LOOPKV_E_INVAL, w + ": " + be);
+  if (opts->num_splits < 0) return fail(LOOPKV_E_INVAL, w + ": num_splits must be >= 0");
+  if (batch->max_seq_len < 0) return fail(LOOPKV_E_INVAL, w + ": negative max_seq_len");
+  if (!std::isfinite(opts->sm_scale)) return fail(LOOPKV_E_INVAL, w + ": sm_scale must be finite");
   if (batch->batch == 0) return LOOPKV_OK;
-  if (!q_bf16 || !out) return fail(LOOPKV_E_INVAL, "decode: NULL query or output");
+  if (!q_bf16 || !out) return fail(LOOPKV_E_INVAL, w + ": NULL query or output");
   if (misaligned(q_bf16, 2) || misaligned(out, 4) || misaligned(opts->mask_bits, 4) ||
       misaligned(opts->counters, 8))
-    return fail(LOOPKV_E_INVAL, "decode: q must be 2-byte, out and mask_bits 4-byte, counters 8-byte aligned");
+    return fail(LOOPKV_E_INVAL, w + ": q must be 2-byte, out and mask_bits 4-byte, counters 8-byte aligned");
   if (!batch->seq_lens || !batch->block_tables)
-    return fail(LOOPKV_E_INVAL, "decode: NULL seq_lens or block_tables");
-  if (batch->max_pages < 1) return fail(LOOPKV_E_INVAL, "decode: max_pages must be >= 1");
+    return fail(LOOPKV_E_INVAL, w + ": NULL seq_lens or block_tables");
+  if (batch->max_pages < 1) return fail(LOOPKV_E_INVAL, w + ": max_pages must be >= 1");
   if (static_cast<int64_t>(batch->max_pages) * plan->P < batch->max_seq_len)
-    return fail(LOOPKV_E_INVAL, "decode: max_pages * page_size < max_seq_len");
-  const WorkspacePlan wp = workspace_plan(batch->batch, plan->H, plan->D, batch->max_seq_len);
-  if (!opts->workspace || opts->workspace_bytes < wp.total)
-    return fail(LOOPKV_E_CAPACITY, "decode: workspace smaller than loopkv_decode_workspace_bytes (" +
-                                       std::to_string(wp.total) + " bytes)");
+    return fail(LOOPKV_E_INVAL, w + ": max_pages * page_size < max_seq_len");
+  const Splits sp = choose_splits(batch->batch, plan->H, batch->max_seq_len,
+                                  batch->sum_seq_lens > 0 ? batch->sum_seq_lens : 0, opts->num_splits);
+  if (sp.S > lkv::kMaxSplits) return fail(LOOPKV_E_INVAL, w + ": max_seq_len needs too many splits");
+  const int mode = decode_mode(src_kind, tau);
+
+  uint8_t* ws;
+  size_t off_counts, off_cand;
+  if (static_scratch) {
+    const CompactScratch cs = compact_scratch(batch->batch, plan->H, plan->D, sp, mode == lkv::kModeSparse);
+    if (cs.total > kStaticScratchBytes)
+      return fail(LOOPKV_E_CAPACITY, w + ": this batch needs " + std::to_string(cs.total) +
+                                         " bytes of scratch, above the library's fixed " +
+                                         std::to_string(kStaticScratchBytes));
+    hipError_t e = hipSuccess;
+    ws = static_scratch_ptr(&e);
+    if (!ws) return fail_hip(e, (w + ": device address of the static scratch").c_str());
+    off_counts = cs.partials;
+    off_cand = cs.partials + cs.counts;
+  } else {
+    const WorkspacePlan wp = workspace_plan(batch->batch, plan->H, plan->D, batch->max_seq_len);
+    if (!opts->workspace || opts->workspace_bytes < wp.total)
+      return fail(LOOPKV_E_CAPACITY, w + ": workspace smaller than loopkv_decode_workspace_bytes (" +
+                                         std::to_string(wp.total) + " bytes)");
+    ws = static_cast<uint8_t*>(opts->workspace);
+    off_counts = wp.partials;
+    off_cand = wp.partials + wp.counts;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (debug_enabled()) {
     const int rc = debug_check(batch, plan->P, mem.num_pages, 0, 0, s);
     if (rc != LOOPKV_OK) return rc;
   }
-  const Splits sp = choose_splits(batch->batch, plan->H, batch->max_seq_len,
-                                  batch->sum_seq_lens > 0 ? batch->sum_seq_lens : 0, opts->num_splits);
-  if (sp.S > lkv::kMaxSplits) return fail(LOOPKV_E_INVAL, "decode: max_seq_len needs too many splits");
-
-  int mode = lkv::kModePlain;
-  if (src_kind == lkv::kKindQ4) {
-    if (tau == 0.0f) mode = lkv::kModeDense;
-    else if (std::isfinite(tau)) mode = lkv::kModeSparse;
-  }
-  uint8_t* ws = static_cast<uint8_t*>(opts->workspace);
   lkv::DecodeArgs a{};
   a.pool = static_cast<const uint8_t*>(mem.pool);
   a.seq_lens = batch->seq_lens;
@@ -500,8 +580,8 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
   a.q = static_cast<const uint16_t*>(q_bf16);
   a.out = out;
   a.partials = reinterpret_cast<float*>(ws);
-  a.cand_count = reinterpret_cast<int32_t*>(ws + wp.partials);
-  a.cand = reinterpret_cast<int2*>(ws + wp.partials + wp.counts);
+  a.cand_count = reinterpret_cast<int32_t*>(ws + off_counts);
+  a.cand = reinterpret_cast<int2*>(ws + off_cand);
   a.mask_bits = opts->mask_bits;
   a.counters = opts->counters;
   a.num_pages = mem.num_pages;
@@ -515,9 +595,36 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
   a.log_tau = (mode == lkv::kModeSparse) ? std::log(tau) : 0.0f;
   a.lay = lkv::make_layout(src_kind, plan->P, plan->D);
   const hipError_t e = lkv::launch_decode(a, batch->batch, mode, s);
-  if (e != hipSuccess) return fail_hip(e, "decode: kernel launch");
+  if (e != hipSuccess) return fail_hip(e, (w + ": kernel launch").c_str());
   g_err.clear();
   return LOOPKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loop, int layer,
+                  const loopkv_batch* batch, const void* q_bf16, float* out,
+                  const loopkv_decode_opts* opts, void* stream) {
+  return decode_impl("decode", plan, cells, loop, layer, batch, q_bf16, out, opts, stream, false);
+}
+
+size_t loopkv_decode_noalloc_bytes(const loopkv_plan* plan, int loop, int layer, int32_t batch,
+                                   int32_t max_seq_len, int32_t sum_seq_lens, int32_t num_splits) {
+  if (!cell_ok(plan, loop, layer) || batch < 0 || max_seq_len < 0 || num_splits < 0) return 0;
+  const size_t c = static_cast<size_t>(loop) * plan->L + layer;
+  const int src_loop = plan->kind[c] == lkv::kKindReuse ? plan->R - 1 : loop;
+  const int src_kind = plan->kind[static_cast<size_t>(src_loop) * plan->L + layer];
+  const Splits sp = choose_splits(batch, plan->H, max_seq_len, sum_seq_lens > 0 ? sum_seq_lens : 0, num_splits);
+  return compact_scratch(batch, plan->H, plan->D, sp, decode_mode(src_kind, plan->tau[c]) == lkv::kModeSparse)
+      .total;
+}
+
+int loopkv_decode_noalloc(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loop, int layer,
+                          const loopkv_batch* batch, const void* q_bf16, float* out,
+                          const loopkv_decode_opts* opts, void* stream) {
+  return decode_impl("decode_noalloc", plan, cells, loop, layer, batch, q_bf16, out, opts, stream, true);
 }
 
 // ---- joint vector quantization across loop steps -------------------------

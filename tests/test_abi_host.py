@@ -336,3 +336,45 @@ def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError, match="device tensor"):
         abi.make_batch(torch.zeros(1, dtype=torch.int32), torch.zeros(1, 4, dtype=torch.int32), max_seq_len=64)
+
+
+def test_noalloc_decode_sizes_and_host_errors():
+    """loopkv_decode_noalloc_bytes is the compact scratch of the chosen split
+    layout (partials, counts, and candidate lists only with a tau mask); a
+    batch above the fixed scratch, and bad arguments, fail before anything
+    touches a device (the addresses below are never dereferenced)."""
+    H, D = 16, 128
+    p = abi.Plan(abi.plan_blob(2, 2, H, D, 32, [[0, 1], [0, 2 - 2]], [[0.01, 0.01], [math.inf, 0.0]]))
+    lib = abi.lib()
+    for B, T in ((1, 64), (4, 3000), (8, 4096), (32, 16384)):
+        S, ln = p.decode_splits(B, T, 0, 0)
+        recs = B * H * S
+        base = _round_up(recs * (D + 4) * 4, 256) + _round_up(recs * 4, 256)
+        cand = _round_up(recs * ln * 8, 256)
+        assert abi.loopkv_decode_noalloc_bytes(p, 0, 0, B, T) == base + cand    # 4-bit, 0 < tau < inf
+        assert abi.loopkv_decode_noalloc_bytes(p, 0, 1, B, T) == base           # 2-bit source
+        assert abi.loopkv_decode_noalloc_bytes(p, 1, 0, B, T) == base           # tau = +inf
+        assert abi.loopkv_decode_noalloc_bytes(p, 1, 1, B, T) == base           # tau = 0
+    assert abi.loopkv_decode_noalloc_bytes(p, 0, 7, 1, 64) == 0
+    assert abi.loopkv_decode_noalloc_bytes(p, 0, 0, -1, 64) == 0
+    assert abi.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert abi.loopkv_decode_noalloc_bytes(p, 0, 0, 32, 16384) > abi.NOALLOC_SCRATCH_BYTES
+
+    pages = 32 * 16384 // 32
+    cells = abi.cell_array(p, {c: (_FakeTensor(0x100000 * (i + 1)), _FakeTensor(0x80000000 + 0x100000 * i),
+                                   pages, 32) for i, c in enumerate([(0, 0), (0, 1), (1, 0), (1, 1)])})
+    lens = _FakeTensor(0x7000, shape=(32,))
+    table = _FakeTensor(0x8000, shape=(32, 512))
+
+    def dec(loop, layer, B=32, T=16384, **kw):
+        b = abi.make_batch(lens, table, max_seq_len=T, batch=B)
+        return lib.loopkv_decode_noalloc(p.handle, ctypes.cast(cells, ctypes.c_void_p), loop, layer,
+                                         ctypes.byref(b), 0x9000, 0xA000, ctypes.byref(abi.make_opts(None, **kw)),
+                                         None)
+
+    assert dec(0, 0) == abi.E_CAPACITY and "scratch" in abi.last_error()
+    assert dec(0, 0, B=0) == abi.OK
+    assert dec(0, 9) == abi.E_INVAL
+    assert dec(0, 0, num_splits=-1) == abi.E_INVAL
+    assert dec(0, 0, sm_scale=math.nan) == abi.E_INVAL
+    p.close()
