@@ -34,8 +34,25 @@ loopvq     joint vector quantization across loop steps and its decode
            ("LoopVQ: Sub 1-bit KV Cache Quantization for Looped
            Transformers", abstract)
 
-Parity status of every function is listed in each module's header.  No
-function here is "parity unpinned": each is pinned by tests under
-``tests/test_oracle_*.py`` to closed forms, brute force, a library routine or
-hand-derived fixtures in ``tests/golden``.
+Parity status of every function is listed in each module's header, with
+the tests under ``tests/`` that pin it to something other than itself:
+
+codec.quantize / f16 rounding  exhaustive fp16 search, exact nearest grid
+                               point (Fractions), half-step bound, goldens
+codec planes / row packing     all 16 codes, all 256 bytes, goldens
+cache.build_cell_cache         per-group codec equality, pure function of
+                               the sequence
+cache.pack_pool / layout       hand-placed bytes: 4-bit over 16-token pages,
+                               2-bit region order with a later key group's
+                               metadata on its own page, the second metadata
+                               slot of 64-token pages; round trips
+attention.decode               SDPA (float64) at tau = 0 and +inf and for
+                               2-bit cells, bucket-mean midpoint, mask size
+                               and nesting, 50-digit mpmath brute force
+attention.ambiguity_band       closed-form inside/outside cases
+planner                        hand-computed one-layer cases, closed forms
+loopvq                         planted codeword, lossless codebook, SDPA
+
+End-to-end values at the workloads' real shapes are pinned only through
+these parts: the pages print no values.
 """

@@ -32,7 +32,8 @@ and tau = +inf against high-plane-only attention, both through
 torch.nn.functional.scaled_dot_product_attention in float64; 2-bit cells the
 same way; the midpoint equals the mean of the four full reconstructions of
 its bucket; reuse equals the source; mask size at most floor(1/tau); masks
-nested in tau; a 50-digit mpmath brute force on tiny inputs.
+nested in tau; a 50-digit mpmath brute force on tiny inputs;
+ambiguity_band by closed-form cases just inside and just outside 1e-3 tau.
 """
 from __future__ import annotations
 

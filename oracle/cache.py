@@ -28,8 +28,10 @@ Readings where the pages are silent:
 * defined bytes are rows and V meta of tokens < T and K meta slots of
   groups holding at least one token; every other byte is unspecified.
 
-Pins: round trip pack -> unpack (tests/test_oracle_cache.py) and the
-hand-placed byte offsets of tests/golden/layout_case.txt.
+Pins (tests/test_oracle_cache.py): round trip pack -> unpack, and the
+hand-placed bytes of tests/golden/layout_case.txt (4-bit, 16-token pages),
+layout_q2_p16.txt (2-bit region order; a later key group's metadata on its
+own first page) and layout_q4_p64.txt (the second key-metadata slot).
 """
 from __future__ import annotations
 

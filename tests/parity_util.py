@@ -6,7 +6,8 @@ the reference side is the CPU oracle.  Both get the same seeded inputs.
 Parity bar:
 * pools: bit-exact on every defined byte;
 * tau masks: bit-exact outside the ambiguity band |p - tau| <= 1e-3 tau,
-  where either decision is correct;
+  where either decision is correct; the band may hold at most
+  16 + flagged/50 token-heads per comparison;
 * outputs: after the oracle adopts the GPU's decisions inside the band,
   max |o_gpu - o_oracle| <= 2e-3 * max |o_oracle| over the compared
   [sequence, head, channel] block of one cell.
@@ -124,6 +125,10 @@ def compare_decode(state, r, l, q, out, mask, host_kv, seqs, lens=None, sm_scale
                 assert not gflags.any(), "2-bit source must not flag tokens"
         og.append(out_h[b])
         oo.append(res["out"])
+    # the band excuses only near-ties: a handful of token-heads, far fewer
+    # than the flags (a widened band would excuse a large share of them)
+    assert band_total <= 16 + flagged // 50, (
+        f"cell ({r},{l}): {band_total} token-heads in the ambiguity band for {flagged} flags")
     og, oo = np.stack(og), np.stack(oo)
     scale = float(np.abs(oo).max()) if oo.size else 0.0
     err = float(np.abs(og - oo).max()) if oo.size else 0.0

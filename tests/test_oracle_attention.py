@@ -192,3 +192,30 @@ def test_mpmath_brute_force_tiny(kind):
         flags = [bool(pt >= tau) if kind == oc.KIND_Q4 else False for pt in p]
         assert r["flags"][0].tolist() == flags
         np.testing.assert_allclose(r["out"][0], np.array(out), rtol=1e-13, atol=1e-13)
+
+
+def test_ambiguity_band_closed_form():
+    """The band where either mask decision is accepted is |p - tau| <= 1e-3 tau
+    (a threshold on a computed float cannot be exact at the boundary): weights
+    5e-4 tau away are inside, 2e-3 tau away outside, on both sides; tau = 0
+    and tau = +inf (no threshold to be near) have an empty band."""
+    for tau in (1e-4, 0.005, 0.02, 0.5):
+        inside = np.array([tau * (1 - 5e-4), tau, tau * (1 + 5e-4), tau * (1 - 9.9e-4), tau * (1 + 9.9e-4)])
+        outside = np.array([tau * (1 - 2e-3), tau * (1 + 2e-3), tau * 0.5, tau * 1.5, 0.0, 1.0])
+        assert oa.ambiguity_band(inside, tau).all(), tau
+        assert not oa.ambiguity_band(outside, tau).any(), tau
+    p = np.array([0.0, 1e-9, 0.3, 1.0])
+    assert not oa.ambiguity_band(p, 0.0).any()
+    assert not oa.ambiguity_band(p, math.inf).any()
+
+
+def test_ambiguity_band_is_rare_at_workload_shapes():
+    """On a realistic (sequence, head) set the band holds a tiny share of the
+    flagged tokens, which is what lets the GPU parity checks bound it."""
+    rng = np.random.default_rng(11)
+    c, q = _make(rng, 4096, 8, 64, oc.KIND_Q4, heavy=40)
+    for tau in (0.002, 0.01):
+        r = oa.decode(c, q, tau)
+        band = oa.ambiguity_band(r["p"], tau)
+        assert r["flags"].sum() > 20
+        assert band.sum() <= 2 + r["flags"].sum() // 50, (tau, band.sum(), r["flags"].sum())

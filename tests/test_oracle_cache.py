@@ -1,6 +1,9 @@
 """Pins of the oracle's cell cache and paged layout (CPU only).
 
-* hand-placed bytes of a head-block (tests/golden/layout_case.txt);
+* hand-placed bytes of head-blocks (tests/golden/layout_case.txt: 4-bit,
+  16-token pages; layout_q2_p16.txt: 2-bit region order and a later key
+  group's metadata on its own first page; layout_q4_p64.txt: the second
+  key-metadata slot of 64-token pages);
 * pack -> unpack round trip for both cell kinds, page sizes 16/32/64,
   shuffled block tables and ragged tails;
 * the cache is a pure function of the sequence: every key group's codes only
@@ -54,6 +57,71 @@ def test_golden_layout_bytes():
     assert n > 20
     # nothing outside page 5 is defined
     assert not defined[0, :5].any() and not defined[0, 6:].any()
+
+
+def _check_golden(name, pool, defined):
+    """Compare against a fixture of (physical page, offset, byte or '-')."""
+    n = 0
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            page, off, val = line.split()
+            page, off = int(page), int(off)
+            if val == "-":
+                assert not defined[0, page, off], (name, page, off)
+            else:
+                assert defined[0, page, off], (name, page, off)
+                assert pool[0, page, off] == int(val), (name, page, off, pool[0, page, off], val)
+            n += 1
+    return n
+
+
+def test_golden_layout_2bit_16_token_pages():
+    """2-bit head-block order (K | V | V meta | K meta) and a second key group
+    whose metadata sits on its own first page, two pages after the first."""
+    P, D, T = 16, 32, 40
+    t = np.arange(T)[:, None, None]
+    d = np.arange(D)[None, None, :]
+    c = oc.CellCache(
+        kind=oc.KIND_Q2,
+        k_codes=((t + d) % 4).astype(np.uint8),
+        k_scale=np.array([[[2.0] * D], [[0.5] * D]], np.float16),
+        k_zero=np.array([[[-1.0] * D], [[3.0] * D]], np.float16),
+        v_codes=np.broadcast_to(t % 4, (T, 1, D)).astype(np.uint8),
+        v_scale=(1.0 + np.arange(T) / 8.0).astype(np.float16).reshape(T, 1, 1),
+        v_zero=np.full((T, 1, 1), -0.5, np.float16),
+    )
+    reg = oc.head_block_regions(oc.KIND_Q2, P, D)
+    assert (reg["k"], reg["v"], reg["v_meta"], reg["k_meta"], reg["HB"]) == (0, 128, 256, 320, 448)
+    pool, defined = oc.pack_pool(c, P, [3, 0, 5], 6)
+    assert _check_golden("layout_q2_p16.txt", pool, defined) > 25
+    assert not defined[0, [1, 2, 4]].any()
+
+
+def test_golden_layout_4bit_64_token_pages():
+    """Two key-metadata slots per 64-token page: group 1 in slot 1 of the
+    first page, group 2 in slot 0 of the next."""
+    P, D, T = 64, 32, 70
+    t = np.arange(T)[:, None, None]
+    d = np.arange(D)[None, None, :]
+    g = np.arange(3)[:, None, None]
+    c = oc.CellCache(
+        kind=oc.KIND_Q4,
+        k_codes=((t + d) % 16).astype(np.uint8),
+        k_scale=np.broadcast_to(0.25 * (g + 1), (3, 1, D)).astype(np.float16),
+        k_zero=np.broadcast_to(-(g + 1.0), (3, 1, D)).astype(np.float16),
+        v_codes=np.full((T, 1, D), 9, np.uint8),
+        v_scale=np.full((T, 1, 1), 1.0, np.float16),
+        v_zero=np.full((T, 1, 1), 0.0, np.float16),
+    )
+    reg = oc.head_block_regions(oc.KIND_Q4, P, D)
+    assert (reg["k_hi"], reg["k_lo"], reg["v_hi"], reg["v_lo"], reg["v_meta"], reg["k_meta"], reg["HB"]) == \
+        (0, 512, 1024, 1536, 2048, 2304, 2560)
+    pool, defined = oc.pack_pool(c, P, [2, 0], 3)
+    assert _check_golden("layout_q4_p64.txt", pool, defined) > 20
+    assert not defined[0, 1].any()
 
 
 @pytest.mark.parametrize("kind", [oc.KIND_Q4, oc.KIND_Q2])
