@@ -17,8 +17,9 @@
  * Conventions for every call
  *   - All pointers documented "device" are HIP device pointers owned by the
  *     caller; "host" pointers are read during the call only.  The library
- *     never allocates, frees or retains device memory.  It owns only the
- *     host-side, immutable plan object.
+ *     never allocates or frees device memory.  It owns the host-side,
+ *     immutable plan object and one fixed device array per GPU, the scratch
+ *     of loopkv_decode_noalloc (part of its loaded code object).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Compute calls are asynchronous on that stream: launch errors are
  *     reported by the return code, faults surface at the caller's next
@@ -30,7 +31,12 @@
  *     and block tables are trusted (an out-of-range entry is undefined
  *     behaviour) unless the environment variable LOOPKV_DEBUG=1 is set, in
  *     which case they are copied to the host and checked first (this
- *     synchronizes the stream).
+ *     synchronizes the stream; an out-of-range entry then fails the call
+ *     with LOOPKV_E_INVAL before any launch).  LOOPKV_LOG=1 prints one line
+ *     per append / decode call to stderr: the cell, its source and mode,
+ *     the split layout and the plan-required bytes of the split pass (from
+ *     sum_seq_lens when given, else for max_seq_len per sequence).  Both
+ *     variables are read on every call.
  *   - The plan is immutable: concurrent calls on different streams are safe
  *     when they write different pools / workspaces.
  *

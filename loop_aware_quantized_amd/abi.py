@@ -11,7 +11,9 @@ import os
 import struct
 from ctypes import c_float, c_int, c_int32, c_int64, c_size_t, c_void_p, c_char_p, POINTER
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libloopkv.so")
+# the in-tree build; LOOPKV_LIB names another build of the same library
+# (e.g. one with host sanitizers) to load instead
+LIB_PATH = os.environ.get("LOOPKV_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libloopkv.so")
 
 OK = 0
 NOOP_REUSE = 1

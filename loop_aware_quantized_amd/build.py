@@ -35,13 +35,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libloopkv.so)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into LIB; always recompiles."""
+# host-code sanitizers (the device code is built as usual): a library for
+# running the CPU tests of the host paths under AddressSanitizer and
+# UndefinedBehaviorSanitizer, loaded with the clang ASan runtime preloaded
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-shared-libasan"]
+SANITIZED_LIB = os.path.join(PKG, "libloopkv_hostsan.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every HIP source into LIB (or, with sanitize, into
+    SANITIZED_LIB with host sanitizers); always recompiles."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError("no HIP sources under " + CSRC)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    target = SANITIZED_LIB if sanitize else LIB
+    tmp = target + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *(SANITIZE_FLAGS if sanitize else []), "-I", INCLUDE, "-I", CSRC, *srcs,
+           "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,9 +63,9 @@ def build(verbose: bool = False) -> str:
                      if "packed-fp32-ops" not in l and l.strip())
     if warn and verbose:
         sys.stderr.write(warn + "\n")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize-host" in sys.argv[1:]))

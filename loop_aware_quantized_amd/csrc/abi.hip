@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -49,12 +50,22 @@ int fail_hip(hipError_t e, const char* what) {
   return LOOPKV_E_HIP;
 }
 
+// LOOPKV_LOG=1: one line per append / decode call on stderr.
+bool log_enabled() {
+  const char* v = std::getenv("LOOPKV_LOG");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+const char* mode_name(int mode) {
+  return mode == lkv::kModeSparse ? "sparse-tau" : mode == lkv::kModeDense ? "dense(tau=0)" : "plain";
+}
+
+// LOOPKV_DEBUG=1: validate device-resident lengths, page tables and slots
+// on the host before a launch (read on every call, so it can be switched
+// within a process).
 bool debug_enabled() {
-  static const bool on = [] {
-    const char* v = std::getenv("LOOPKV_DEBUG");
-    return v && v[0] == '1';
-  }();
-  return on;
+  const char* v = std::getenv("LOOPKV_DEBUG");
+  return v && v[0] == '1' && v[1] == '\0';
 }
 
 int32_t rd_i32(const uint8_t* p) {
@@ -438,6 +449,9 @@ int loopkv_append(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
   a.max_pages = batch->max_pages;
   a.n_new = n_new;
   a.lay = lkv::make_layout(plan->kind[c], plan->P, plan->D);
+  if (log_enabled())
+    std::fprintf(stderr, "[loopkv] append cell (%d,%d) %s batch=%d n_new=%d max_seq_len=%d\n", loop, layer,
+                 plan->kind[c] == lkv::kKindQ4 ? "4-bit" : "2-bit", batch->batch, n_new, batch->max_seq_len);
   const hipError_t e = lkv::launch_append(a, batch->batch, s);
   if (e != hipSuccess) return fail_hip(e, "append: kernel launch");
   g_err.clear();
@@ -594,6 +608,21 @@ int decode_impl(const char* who, const loopkv_plan* plan, const loopkv_cell_mem*
   a.sm_scale = opts->sm_scale;
   a.log_tau = (mode == lkv::kModeSparse) ? std::log(tau) : 0.0f;
   a.lay = lkv::make_layout(src_kind, plan->P, plan->D);
+  if (log_enabled()) {
+    // plan-required bytes of the split pass: per token-head D (4-bit source:
+    // both key planes, high value plane, metadata) or 3D/4 (2-bit), plus the
+    // low plane D/4 when tau = 0
+    const int64_t per = (src_kind == lkv::kKindQ4 ? plan->D : 3 * plan->D / 4) +
+                        (mode == lkv::kModeDense ? plan->D / 4 : 0);
+    const bool hint = batch->sum_seq_lens > 0;
+    const int64_t tokens = hint ? batch->sum_seq_lens : static_cast<int64_t>(batch->batch) * batch->max_seq_len;
+    std::fprintf(stderr,
+                 "[loopkv] %s cell (%d,%d) src (%d,%d) %s %s tau=%g batch=%d max_seq_len=%d splits=%d x %d "
+                 "tokens, required split-pass bytes %s%lld\n",
+                 who, loop, layer, src_loop, layer, src_kind == lkv::kKindQ4 ? "4-bit" : "2-bit", mode_name(mode),
+                 static_cast<double>(tau), batch->batch, batch->max_seq_len, sp.S, sp.len, hint ? "" : "<= ",
+                 static_cast<long long>(tokens * plan->H * per));
+  }
   const hipError_t e = lkv::launch_decode(a, batch->batch, mode, s);
   if (e != hipSuccess) return fail_hip(e, (w + ": kernel launch").c_str());
   g_err.clear();

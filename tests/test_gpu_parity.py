@@ -341,20 +341,24 @@ def test_many_short_ragged_pairs():
 def test_graph_replay_matches_eager():
     """Appends and decodes captured in one HIP graph give, on every replay,
     the same bytes as the same calls made eagerly (eager work and
-    synchronizations run between the replays)."""
+    synchronizations run between the replays), and every replay's outputs
+    and masks match the oracle on the sequence as it stands after that
+    replay's append."""
     w = wl.Workload("graph", 180, batch=3, loops=2, layers=2, heads=4, head_dim=128, page=16,
                     ctx=700, heavy_frac=0.01)
     kinds, taus = [[Q4, Q2], [Q4, Q4]], [[0.01, 0.01], [0.0, math.inf]]
     n_steps = 4
     st_e = runner.CacheState(w, DEV, kinds, taus, extra_tokens=n_steps)
     st_g = runner.CacheState(w, DEV, kinds, taus, extra_tokens=n_steps)
+    kept = None
     for st in (st_e, st_g):
         for c in st.stored:
             st.pools[c].zero_()     # unwritten bytes compare equal too
-        st.prefill()
+        kept = st.prefill({c: set(range(w.batch)) for c in st.stored})
     cells = [(r, l) for r in range(2) for l in range(2)]
     qs = {c: wl.cell_query(w, st_e.cell_index(*c), DEV)[1] for c in cells}
     new = {c: wl.append_kv(w, st_e.cell_index(*c), 0, 1, DEV) for c in st_e.stored}
+    new_host = {c: (wl.bf16_bits(k), wl.bf16_bits(v)) for c, (k, v) in new.items()}   # [B][1][H][D]
     lens0 = torch.from_numpy(st_e.lens0.astype(np.int32)).to(DEV)
 
     def run(st, lens_app, lens_dec, outs, masks):
@@ -391,7 +395,15 @@ def test_graph_replay_matches_eager():
             assert torch.equal(masks_g[i], masks_e[i]), (step, cells[i])
         for c in st_e.stored:
             assert torch.equal(st_g.pools[c], st_e.pools[c]), (step, c)
-        say(f"  replay {step}: {len(cells)} cells bit-identical to eager")
+        # the oracle on each sequence's tokens so far: prefill, then the same
+        # appended token once per replay
+        host = {c: {b: tuple(np.concatenate([kept[c][b][i]] + [new_host[c][i][b]] * (step + 1))
+                             for i in range(2)) for b in range(w.batch)} for c in st_e.stored}
+        lens_now = st_e.lens0 + step + 1
+        for i, (r, l) in enumerate(cells):
+            src = oa.resolve_source(st_g.kinds, r, l)
+            compare_decode(st_g, r, l, qs[(r, l)], outs_g[i], masks_g[i], host[src], range(w.batch), lens=lens_now)
+        say(f"  replay {step}: {len(cells)} cells bit-identical to eager and within the oracle's bound")
 
 
 def test_decode_is_deterministic():
@@ -477,3 +489,44 @@ def test_append_ragged_lengths_and_staging():
     for l in range(2):
         q, out, mask, _ = _decode(st, 0, l)
         compare_decode(st, 0, l, q, out, mask, kept[(0, l)], range(w.batch))
+
+
+def test_debug_checks_and_log_lines(capfd, monkeypatch):
+    """LOOPKV_LOG=1 prints one line per call (cell, source, mode, split
+    layout, required bytes); LOOPKV_DEBUG=1 rejects an out-of-range page-table
+    entry and a length above max_seq_len with LOOPKV_E_INVAL before anything
+    is launched (the output keeps its sentinel).  The corrupted case decodes
+    a 2-bit cell, whose kernels read the pool only through bounds-checked
+    buffer loads."""
+    w = wl.Workload("debug", 260, batch=2, loops=1, layers=2, heads=2, head_dim=64, page=16, ctx=200,
+                    heavy_frac=0.01)
+    st = runner.CacheState(w, DEV, [[Q4, Q2]], [[0.01, 0.01]], lengths=[200, 90])
+    kept = st.prefill({c: {0, 1} for c in st.stored})
+    torch.cuda.synchronize()
+    capfd.readouterr()
+    monkeypatch.setenv("LOOPKV_LOG", "1")
+    q, out, mask, _ = _decode(st, 0, 0)
+    err = capfd.readouterr().err
+    monkeypatch.delenv("LOOPKV_LOG")
+    line = [x for x in err.splitlines() if x.startswith("[loopkv] decode cell (0,0)")]
+    assert line and "4-bit sparse-tau" in line[0] and "splits=" in line[0] and "bytes" in line[0], err
+    compare_decode(st, 0, 0, q, out, mask, kept[(0, 0)], range(2))
+
+    monkeypatch.setenv("LOOPKV_DEBUG", "1")
+    q, out, mask, _ = _decode(st, 0, 1)           # valid tables pass the check
+    compare_decode(st, 0, 1, q, out, mask, kept[(0, 1)], range(2))
+    bad = st.block_tables.clone()
+    bad[1, 2] = st.num_pages                      # one past the pool
+    sentinel = torch.full((w.batch, w.heads, w.head_dim), float("nan"), device=DEV)
+    opts = abi.make_opts(st.workspace)
+    with pytest.raises(abi.LoopKVError) as e:
+        abi.loopkv_decode(st.plan, st.cells, 0, 1, abi.make_batch(st.lens, bad, st.max_seq_len), q, sentinel, opts)
+    assert e.value.code == abi.E_INVAL and "block_tables[1][2]" in e.value.message
+    long_lens = torch.tensor([200, st.max_seq_len + 1], dtype=torch.int32, device=DEV)
+    with pytest.raises(abi.LoopKVError) as e:
+        abi.loopkv_decode(st.plan, st.cells, 0, 1, abi.make_batch(long_lens, st.block_tables, st.max_seq_len), q,
+                          sentinel, opts)
+    assert e.value.code == abi.E_INVAL and "seq_lens[1]" in e.value.message
+    torch.cuda.synchronize()
+    assert torch.isnan(sentinel).all(), "nothing may be launched after a failed check"
+    monkeypatch.delenv("LOOPKV_DEBUG")
