@@ -132,16 +132,31 @@ size_t loopkv_decode_workspace_bytes(const loopkv_plan* plan, int32_t batch,
 
 /* The split layout loopkv_decode uses for a batch with these host fields
  * (batch, max_seq_len, sum_seq_lens as in loopkv_batch) and num_splits
- * (0 = automatic): out[0] = splits per (sequence, head), out[1] = tokens per
- * split.  Every layout has out[1] a multiple of 64, out[1] <= 4096,
- * out[1] <= max_seq_len rounded up to 64, out[0] <= 2048 and
- * out[0] * out[1] >= max_seq_len; the workspace size above holds the
+ * (0 = automatic), for a cell with a tau mask or none: out[0] = partial
+ * records per (sequence, head) (the splits of a uniform layout), out[1] =
+ * tokens per split (per wave range of a streamed layout; see
+ * loopkv_decode_layout).  Every layout has out[1] a multiple of 64,
+ * out[1] <= 4096, out[1] <= max_seq_len rounded up to 64, out[0] <= 2048
+ * and out[0] * out[1] >= max_seq_len; the workspace size above holds the
  * partial records and candidate lists of any such layout.  The automatic
  * choice depends on the current device's compute-unit count (256 when no
  * device is visible).  Errors: LOOPKV_E_INVAL (NULL argument, negative
  * sizes, or a num_splits / max_seq_len that needs more than 2048 splits). */
 int loopkv_decode_splits(const loopkv_plan* plan, int32_t batch, int32_t max_seq_len,
                          int32_t sum_seq_lens, int32_t num_splits, int32_t out[2]);
+
+/* The split layout loopkv_decode uses for cell (loop, layer) and these host
+ * fields: out[0] = 0 for a uniform layout (every (sequence, head) cut into
+ * out[1] splits of out[2] tokens, as loopkv_decode_splits reports) or 1 for
+ * a streamed one (out[3] waves, each taking an equal range of out[2] / 64
+ * of the pairs' 64-token tiles laid end to end, sequence-major; a pair gets
+ * one partial record per wave whose range meets it, at most out[1]).
+ * Streamed layouts serve ragged batches (a length sum below 85% of
+ * batch * max_seq_len) of at most 256 sequences with a tau mask or none
+ * (not tau = 0); every wave is then busy for the same time.  Errors:
+ * LOOPKV_E_INVAL as loopkv_decode_splits, or a bad cell. */
+int loopkv_decode_layout(const loopkv_plan* plan, int loop, int layer, int32_t batch, int32_t max_seq_len,
+                         int32_t sum_seq_lens, int32_t num_splits, int32_t out[4]);
 
 /* Memory of one cell; an array of R*L of these is indexed [loop*L + layer].
  * REUSE cells may leave everything NULL / 0. */

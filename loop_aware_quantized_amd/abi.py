@@ -44,6 +44,7 @@ _SIGNATURES = {
     "loopkv_append": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
     "loopkv_decode": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "loopkv_decode_noalloc_bytes": (c_size_t, [c_void_p, c_int, c_int, c_int32, c_int32, c_int32, c_int32]),
+    "loopkv_decode_layout": (c_int, [c_void_p, c_int, c_int, c_int32, c_int32, c_int32, c_int32, POINTER(c_int32)]),
     "loopkv_decode_noalloc": (c_int, [c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p]),
     "loopkv_profile_enable": (c_int, [c_int]),
@@ -266,6 +267,14 @@ def loopkv_decode(plan: Plan, cells, loop: int, layer: int, batch: Batch, q, out
     return _check(lib().loopkv_decode(plan.handle, ctypes.cast(cells, c_void_p), loop, layer,
                                       ctypes.byref(batch), _ptr(q), _ptr(out), ctypes.byref(opts),
                                       _stream_handle(stream)))
+
+
+def loopkv_decode_layout(plan: Plan, loop: int, layer: int, batch: int, max_seq_len: int, sum_seq_lens: int = 0,
+                         num_splits: int = 0):
+    """(streamed, records per pair, tokens per split or wave range, waves or 0) of a decode."""
+    out = (c_int32 * 4)()
+    _check(lib().loopkv_decode_layout(plan.handle, loop, layer, batch, max_seq_len, sum_seq_lens, num_splits, out))
+    return tuple(out)
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20

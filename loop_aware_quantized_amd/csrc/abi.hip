@@ -111,10 +111,24 @@ const char* batch_error(const loopkv_batch* b) {
   return nullptr;
 }
 
-// Split plan for `pairs` (sequence, head) pairs of at most t_max tokens.
+// Split layout of a decode.  Uniform: S splits of len tokens per (sequence,
+// head).  Streamed: `waves` waves each take tpw tiles of the pairs' tiles
+// laid end to end; S is the partial records a pair can have, len = tpw * 64
+// the longest range.  cand_stride: candidate entries per pair.
 struct Splits {
   int S, len;
+  bool streamed = false;
+  int tpw = 0, waves = 0;
+  int64_t cand_stride = 0;
 };
+
+Splits uniform(int64_t tm, int64_t len) {
+  Splits sp;
+  sp.S = static_cast<int>((tm + len - 1) / len);
+  sp.len = static_cast<int>(len);
+  sp.cand_stride = static_cast<int64_t>(sp.S) * len;
+  return sp;
+}
 
 // Split plan for `batch` sequences x `heads` of at most t_max tokens (sum
 // of lengths t_sum when known, else 0).  One wave runs per non-empty split.
@@ -127,7 +141,36 @@ struct Splits {
 // kMaxSplits; a requested count gives splits of ceil(t_max / count) tokens
 // rounded up to a tile.  No split exceeds kMaxSplitLen or the longest
 // sequence rounded up to a tile.
-Splits choose_splits(int64_t batch, int64_t heads, int t_max, int64_t t_sum, int requested) {
+// Streamed layout for a ragged batch: one round of waves (12 per compute
+// unit) with equal ranges of the pairs' tiles laid end to end, so that every
+// wave is busy for about the same time whatever the lengths.  Ranges hold
+// at least 4 tiles and at most a split's 4096 tokens (more waves than one
+// round otherwise).  Needs the length sum, at most kMaxStreamedBatch
+// sequences, and records per pair within the workspace's split capacity.
+bool streamed_layout(int64_t batch, int64_t heads, int64_t tm, int64_t t_sum, int64_t slots, Splits* out) {
+  if (t_sum <= 0 || batch > lkv::kMaxStreamedBatch) return false;
+  const int64_t tiles_ub = heads * ((t_sum + lkv::kTile - 1) / lkv::kTile + batch);   // >= the real count
+  if (tiles_ub > (int64_t{1} << 30)) return false;
+  int64_t tpw = std::max<int64_t>(4, (tiles_ub + slots - 1) / slots);
+  tpw = std::min<int64_t>(tpw, lkv::kMaxSplitLen / lkv::kTile);
+  const int64_t waves = (tiles_ub + tpw - 1) / tpw;
+  const int64_t pair_tiles = (tm + lkv::kTile - 1) / lkv::kTile;
+  const int64_t recs = (pair_tiles + tpw - 1) / tpw + 1;   // a pair's tiles meet at most this many ranges
+  const int64_t s_cap = std::min<int64_t>(lkv::kMaxSplits, pair_tiles);
+  if (recs > s_cap || waves > 0x7fffffff) return false;
+  out->S = static_cast<int>(recs);
+  out->len = static_cast<int>(tpw * lkv::kTile);
+  out->streamed = true;
+  out->tpw = static_cast<int>(tpw);
+  out->waves = static_cast<int>(waves);
+  out->cand_stride = round_up(tm, lkv::kTile);
+  return true;
+}
+
+// stream_ok: the decode mode has a streamed kernel variant at one round of
+// 12 waves per compute unit (the tau = 0 variant needs more registers)
+Splits choose_splits(int64_t batch, int64_t heads, int t_max, int64_t t_sum, int requested,
+                     bool stream_ok = true) {
   const int64_t tm = std::max<int64_t>(t_max, 1);
   const int64_t pairs = std::max<int64_t>(batch * heads, 1);
   const int64_t slots = static_cast<int64_t>(cu_count()) * 12;
@@ -135,9 +178,12 @@ Splits choose_splits(int64_t batch, int64_t heads, int t_max, int64_t t_sum, int
   if (requested > 0) {
     len = round_up((tm + requested - 1) / requested, lkv::kTile);
     len = std::min<int64_t>(len, lkv::kMaxSplitLen);
-    return {static_cast<int>((tm + len - 1) / len), static_cast<int>(len)};
+    return uniform(tm, len);
   }
-  if (t_sum > 0 && t_sum * 100 < tm * batch * 85) {
+  const bool ragged = t_sum > 0 && t_sum * 100 < tm * batch * 85;
+  Splits st;
+  if (ragged && stream_ok && streamed_layout(batch, heads, tm, t_sum, slots, &st)) return st;
+  if (ragged) {
     len = round_up((t_sum * heads + 3 * slots - 1) / (3 * slots), lkv::kTile);
   } else {
     const int64_t s0 = (slots + pairs - 1) / pairs;
@@ -151,8 +197,7 @@ Splits choose_splits(int64_t batch, int64_t heads, int t_max, int64_t t_sum, int
   // stride relies on it
   len = std::min<int64_t>(len, round_up(tm, lkv::kTile));
   len = std::min<int64_t>(len, lkv::kMaxSplitLen);
-  const int64_t S = (tm + len - 1) / len;
-  return {static_cast<int>(S), static_cast<int>(len)};
+  return uniform(tm, len);
 }
 
 struct WorkspacePlan {
@@ -510,7 +555,7 @@ CompactScratch compact_scratch(int64_t batch, int64_t H, int64_t D, const Splits
   CompactScratch c;
   c.partials = static_cast<size_t>(round_up(recs * (D + lkv::kPartialPad) * 4, 256));
   c.counts = static_cast<size_t>(round_up(recs * 4, 256));
-  c.cand = sparse ? static_cast<size_t>(round_up(recs * sp.len * 8, 256)) : 0;
+  c.cand = sparse ? static_cast<size_t>(round_up(batch * H * sp.cand_stride * 8, 256)) : 0;
   c.total = c.partials + c.counts + c.cand;
   return c;
 }
@@ -555,10 +600,11 @@ int decode_impl(const char* who, const loopkv_plan* plan, const loopkv_cell_mem*
   if (batch->max_pages < 1) return fail(LOOPKV_E_INVAL, w + ": max_pages must be >= 1");
   if (static_cast<int64_t>(batch->max_pages) * plan->P < batch->max_seq_len)
     return fail(LOOPKV_E_INVAL, w + ": max_pages * page_size < max_seq_len");
-  const Splits sp = choose_splits(batch->batch, plan->H, batch->max_seq_len,
-                                  batch->sum_seq_lens > 0 ? batch->sum_seq_lens : 0, opts->num_splits);
-  if (sp.S > lkv::kMaxSplits) return fail(LOOPKV_E_INVAL, w + ": max_seq_len needs too many splits");
   const int mode = decode_mode(src_kind, tau);
+  const Splits sp = choose_splits(batch->batch, plan->H, batch->max_seq_len,
+                                  batch->sum_seq_lens > 0 ? batch->sum_seq_lens : 0, opts->num_splits,
+                                  mode != lkv::kModeDense);
+  if (sp.S > lkv::kMaxSplits) return fail(LOOPKV_E_INVAL, w + ": max_seq_len needs too many splits");
 
   uint8_t* ws;
   size_t off_counts, off_cand;
@@ -603,7 +649,13 @@ int decode_impl(const char* who, const loopkv_plan* plan, const loopkv_cell_mem*
   a.max_pages = batch->max_pages;
   a.S = sp.S;
   a.split_len = sp.len;
-  a.graded_priority = static_cast<int64_t>(sp.S) * plan->H * batch->batch <= static_cast<int64_t>(cu_count()) * 12;
+  a.streamed = sp.streamed ? 1 : 0;
+  a.tiles_per_wave = sp.tpw;
+  a.waves = sp.waves;
+  a.batch = batch->batch;
+  a.cand_stride = static_cast<int32_t>(sp.cand_stride);
+  const int64_t waves = sp.streamed ? sp.waves : static_cast<int64_t>(sp.S) * plan->H * batch->batch;
+  a.graded_priority = waves <= static_cast<int64_t>(cu_count()) * 12;
   a.mask_words = (batch->max_seq_len + 31) / 32;
   a.sm_scale = opts->sm_scale;
   a.log_tau = (mode == lkv::kModeSparse) ? std::log(tau) : 0.0f;
@@ -639,15 +691,34 @@ int loopkv_decode(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loo
   return decode_impl("decode", plan, cells, loop, layer, batch, q_bf16, out, opts, stream, false);
 }
 
+int loopkv_decode_layout(const loopkv_plan* plan, int loop, int layer, int32_t batch, int32_t max_seq_len,
+                         int32_t sum_seq_lens, int32_t num_splits, int32_t out[4]) {
+  if (!cell_ok(plan, loop, layer) || !out) return fail(LOOPKV_E_INVAL, "decode_layout: bad cell or NULL out");
+  if (batch < 0 || max_seq_len < 0 || num_splits < 0)
+    return fail(LOOPKV_E_INVAL, "decode_layout: negative batch, max_seq_len or num_splits");
+  const size_t c = static_cast<size_t>(loop) * plan->L + layer;
+  const int src_loop = plan->kind[c] == lkv::kKindReuse ? plan->R - 1 : loop;
+  const int src_kind = plan->kind[static_cast<size_t>(src_loop) * plan->L + layer];
+  const Splits sp = choose_splits(batch, plan->H, max_seq_len, sum_seq_lens > 0 ? sum_seq_lens : 0, num_splits,
+                                  decode_mode(src_kind, plan->tau[c]) != lkv::kModeDense);
+  if (sp.S > lkv::kMaxSplits) return fail(LOOPKV_E_INVAL, "decode_layout: max_seq_len needs too many splits");
+  out[0] = sp.streamed ? 1 : 0;
+  out[1] = sp.S;
+  out[2] = sp.len;
+  out[3] = sp.streamed ? sp.waves : 0;
+  return LOOPKV_OK;
+}
+
 size_t loopkv_decode_noalloc_bytes(const loopkv_plan* plan, int loop, int layer, int32_t batch,
                                    int32_t max_seq_len, int32_t sum_seq_lens, int32_t num_splits) {
   if (!cell_ok(plan, loop, layer) || batch < 0 || max_seq_len < 0 || num_splits < 0) return 0;
   const size_t c = static_cast<size_t>(loop) * plan->L + layer;
   const int src_loop = plan->kind[c] == lkv::kKindReuse ? plan->R - 1 : loop;
   const int src_kind = plan->kind[static_cast<size_t>(src_loop) * plan->L + layer];
-  const Splits sp = choose_splits(batch, plan->H, max_seq_len, sum_seq_lens > 0 ? sum_seq_lens : 0, num_splits);
-  return compact_scratch(batch, plan->H, plan->D, sp, decode_mode(src_kind, plan->tau[c]) == lkv::kModeSparse)
-      .total;
+  const int mode = decode_mode(src_kind, plan->tau[c]);
+  const Splits sp = choose_splits(batch, plan->H, max_seq_len, sum_seq_lens > 0 ? sum_seq_lens : 0, num_splits,
+                                  mode != lkv::kModeDense);
+  return compact_scratch(batch, plan->H, plan->D, sp, mode == lkv::kModeSparse).total;
 }
 
 int loopkv_decode_noalloc(const loopkv_plan* plan, const loopkv_cell_mem* cells, int loop, int layer,

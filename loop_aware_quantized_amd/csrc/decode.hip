@@ -196,15 +196,43 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < kCPL; ++c) v0[u][c] = rec[lane + 64 * c];
   }
+  // streamed layout: tiles (all heads) of the sequences before this one
+  int tiles_before = 0;
+  if (a.streamed) {
+#pragma unroll
+    for (int k = 0; k < kMaxStreamedBatch / 64; ++k) {
+      const int bb = lane + 64 * k;
+      tiles_before += bb < b ? a.H * ((max(a.seq_lens[bb], 0) + kTile - 1) / kTile) : 0;
+    }
+  }
   const int T = a.seq_lens[b];
+  uint32_t* mrow = a.mask_bits ? a.mask_bits + pair * a.mask_words : nullptr;
   if (T <= 0) {
     for (int d = lane; d < D; d += 64) outp[d] = 0.0f;
+    // no split of an empty pair runs in a streamed layout: its row is cleared here
+    if (mrow)
+      for (int w = lane; w < a.mask_words; w += 64) mrow[w] = 0u;
     return;
   }
-  // lengths above max_seq_len break the caller's contract; never read past S
-  const int S_used = min((T + a.split_len - 1) / a.split_len, a.S);
-  // the row was cleared by the split kernel (first split of the pair)
-  uint32_t* mrow = a.mask_bits ? a.mask_bits + pair * a.mask_words : nullptr;
+  // Records of the pair and the first token of each.  Uniform: record r is
+  // split r.  Streamed: the pair's tiles start at tile0 of the end-to-end
+  // order, and record r is the part of wave (tile0 / tpw + r)'s range in it.
+  const int tpw = a.tiles_per_wave;
+  int tile0 = 0, S_used;
+  if (a.streamed) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) tiles_before += __shfl_xor(tiles_before, o, 64);
+    const int nb = (T + kTile - 1) / kTile;
+    tile0 = tiles_before + h * nb;
+    S_used = min((tile0 + nb - 1) / tpw - tile0 / tpw + 1, a.S);
+  } else {
+    // lengths above max_seq_len break the caller's contract; never read past S
+    S_used = min((T + a.split_len - 1) / a.split_len, a.S);
+  }
+  auto rec_start = [&](int r) -> int {
+    return a.streamed ? max(0, (tile0 / tpw + r) * tpw - tile0) * kTile : r * a.split_len;
+  };
+  // the row was cleared by the split kernel (the split holding token 0)
   const float m_l = lane < S_used ? ml_raw.x : -INFINITY;
   const float l_l = lane < S_used ? ml_raw.y : 0.0f;
   const int cnt0 = lane < S_used ? cnt_raw : 0;
@@ -335,7 +363,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
               else lo = mid + 1;
             }
             const int before = lo ? pre[lo - 1] : 0;
-            c[u] = a.cand[(pair * a.S + i0 + lo) * a.split_len + (k - before)];
+            c[u] = a.cand[pair * a.cand_stride + rec_start(i0 + lo) + (k - before)];
           }
         }
 #pragma unroll
@@ -379,8 +407,13 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   for (int d = lane; d < D; d += 64) outp[d] = o_s[d];
 }
 
+// One split of one (sequence, head): tokens [start, end) of sequence b
+// (length T), head h; its partial record is number rec of the pair, and
+// `first` marks the split holding the pair's first token (which owns the
+// pair's mask row).
 template <int D, int KIND, int MODE>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+__device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, const int h, const int T,
+                                              const int start, const int end, const int rec, const bool first) {
   constexpr int kNJ = D / kGroup;       // value channel groups
   constexpr int kSlots = 64 / kNJ;      // tokens per value step
   constexpr int kSubs = kTile / kSlots; // value steps per tile
@@ -402,14 +435,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   __shared__ int2 cbuf[kSparse ? kCandCap : 1];   // candidate (token, score bits)
 
   const int lane = threadIdx.x;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int H = a.H;
   const CellLayout L = a.lay;
-  const int T = a.seq_lens[b];
-  const int start = split * a.split_len;
-  const int end = min(start + a.split_len, T);
   const int64_t pair = static_cast<int64_t>(b) * H + h;
-  float* part = a.partials + (pair * a.S + split) * (D + kPartialPad);
+  float* part = a.partials + (pair * a.S + rec) * (D + kPartialPad);
   // page size is a power of two; splits and tiles start on page boundaries
   const int lgP = __builtin_ctz(static_cast<unsigned>(L.P));
   const int pmask = L.P - 1;
@@ -433,7 +462,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int c = 0; c < D / 64; ++c) q_raw[c] = bf16_to_f32(a.q[pair * D + lane + 64 * c]);
 
-  if (split == 0 && a.mask_bits) {
+  if (first && a.mask_bits) {
     // the first split owns the pair's mask row: cleared here (all ones up to
     // T for tau = 0); the merge kernel, launched after, sets the flag bits
     uint32_t* mrow = a.mask_bits + pair * a.mask_words;
@@ -557,7 +586,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // Candidates collect in LDS (cbuf, n_buf entries).  When a tile's new ones
   // do not fit, the buffer is first re-tested against the running threshold,
   // which only rises; if still full it spills to the global list (n_glob).
-  int2* cand_list = a.cand + (pair * a.S + split) * a.split_len;
+  int2* cand_list = a.cand + pair * a.cand_stride + start;
   int n_buf = 0, n_glob = 0;
   auto compact = [&](float th) {
     int n = 0;
@@ -833,15 +862,85 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     // final test against this split's own LSE (still <= the global one)
     compact(ref + logf(lsum) + a.log_tau - 1e-3f);
     spill();
-    if (lane == 0) a.cand_count[pair * a.S + split] = n_glob;
+    if (lane == 0) a.cand_count[pair * a.S + rec] = n_glob;
+  }
+}
+
+template <int D, int KIND, int MODE>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int T = a.seq_lens[b];
+  const int start = split * a.split_len;
+  split_segment<D, KIND, MODE>(a, b, h, T, start, min(start + a.split_len, T), split, split == 0);
+}
+
+// Streamed layout: wave w takes its range of the pairs' tiles laid end to
+// end (sequence-major, then head), one split segment per pair it meets.  The tile counts of all sequences (B <= 256)
+// are scanned once into LDS.
+template <int D, int KIND, int MODE>
+__global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs a) {
+  __shared__ int seq_first[kMaxStreamedBatch + 1];   // first tile of each sequence, then the total
+  const int lane = threadIdx.x;
+  const int H = a.H;
+  int tl[4];
+  int own = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int bb = 4 * lane + k;
+    const int T = bb < a.batch ? max(a.seq_lens[bb], 0) : 0;
+    tl[k] = H * ((T + kTile - 1) / kTile);   // tiles of all heads of sequence bb
+    own += tl[k];
+  }
+  int incl = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  int run = incl - own;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    seq_first[4 * lane + k] = run;
+    run += tl[k];
+  }
+  if (lane == 63) seq_first[kMaxStreamedBatch] = run;
+  __syncthreads();
+  const int total = seq_first[kMaxStreamedBatch];
+  const int tpw = a.tiles_per_wave;
+  const int w = blockIdx.x;
+  int t = w * tpw;
+  const int t_end = min(t + tpw, total);
+  while (t < t_end) {
+    // the sequence holding tile t: the last b < B with seq_first[b] <= t
+    int lo = 0, hi = a.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seq_first[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    const int b = __builtin_amdgcn_readfirstlane(lo);
+    const int first_tile = __builtin_amdgcn_readfirstlane(seq_first[b]);
+    const int T = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+    const int nb = (T + kTile - 1) / kTile;              // tiles per head
+    const int h = (t - first_tile) / nb;
+    const int j = t - first_tile - h * nb;               // tile index within the pair
+    const int seg = min(nb - j, t_end - t);
+    const int pair_first = first_tile + h * nb;
+    split_segment<D, KIND, MODE>(a, b, h, T, j * kTile, min((j + seg) * kTile, T), w - pair_first / tpw, j == 0);
+    __syncthreads();                                     // LDS of this segment is free again
+    t += seg;
   }
 }
 
 template <int D, int KIND, int MODE>
 hipError_t launch_typed(const DecodeArgs& a, int batch, hipStream_t stream) {
   const ProfEvents es = prof_events(kClassSplit);
-  hipExtLaunchKernelGGL((decode_split_kernel<D, KIND, MODE>), dim3(a.S, a.H, batch), dim3(64), 0, stream,
-                        es.start, es.stop, 0, a);
+  if (a.streamed)
+    hipExtLaunchKernelGGL((decode_stream_kernel<D, KIND, MODE>), dim3(a.waves), dim3(64), 0, stream, es.start,
+                          es.stop, 0, a);
+  else
+    hipExtLaunchKernelGGL((decode_split_kernel<D, KIND, MODE>), dim3(a.S, a.H, batch), dim3(64), 0, stream,
+                          es.start, es.stop, 0, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const ProfEvents em = prof_events(kClassMerge);

@@ -46,7 +46,23 @@ struct DecodeArgs {
   float sm_scale;
   float log_tau;                     // ln(tau) for the candidate / flag test
   CellLayout lay;
+  // Split layout.  Uniform (streamed == 0): the grid is (S, H, B) and split
+  // k of a (sequence, head) covers tokens [k * split_len, (k + 1) *
+  // split_len).  Streamed: the (sequence, head) pairs' 64-token tiles are
+  // laid end to end (sequence-major, then head) and wave w of a 1-D grid
+  // takes tiles [w * tiles_per_wave, (w + 1) * tiles_per_wave); each pair it
+  // touches gets one partial record, numbered from the first wave that
+  // touches the pair.  S: partial records per pair; cand_stride: candidate
+  // entries per pair (a record's list starts at its first token's offset).
+  int32_t streamed;
+  int32_t tiles_per_wave;
+  int32_t waves;                     // streamed: the grid
+  int32_t batch;
+  int32_t cand_stride;
 };
+
+// Sequences of a streamed layout (each wave scans all their lengths).
+constexpr int kMaxStreamedBatch = 256;
 
 // mode of a decode launch
 enum DecodeMode : int {

@@ -294,10 +294,11 @@ def _rup(x, m):
 def test_decode_splits_fit_the_workspace(H, D):
     """Every split layout (automatic, for uniform and ragged length hints,
     or requested) has whole 64-token tiles, at most 4096 tokens per split
-    and no split longer than the longest sequence, covers max_seq_len, and
-    fits the workspace loopkv_decode_workspace_bytes reserves: per (sequence,
-    head) S partial records of D + 4 floats, S candidate counts and S lists
-    of split-length 8-byte entries.  Among the cases: 4096 x 16 short ragged
+    and, when uniform, no split longer than the longest sequence; it covers
+    max_seq_len and fits the workspace loopkv_decode_workspace_bytes
+    reserves: per (sequence, head) S partial records of D + 4 floats, S
+    candidate counts and S lists of split-length 8-byte entries (streamed
+    layouts: one list slot per token of the longest sequence).  Among the cases: 4096 x 16 short ragged
     sequences, where the ragged rule alone would ask for splits 4.5x longer
     than the sequences."""
     p = abi.Plan(_blob(H=H, D=D, kinds=[[0, 2], [1, 0]]))
@@ -314,12 +315,24 @@ def test_decode_splits_fit_the_workspace(H, D):
                         # only a requested count can ask for too many splits
                         assert req > 0 and -(-tm // min(4096, _rup(-(-max(tm, 1) // req), 64))) > 2048
                         continue
+                    streamed, S2, ln2, waves = abi.loopkv_decode_layout(p, 0, 0, batch, tm, t_sum, req)
+                    assert (S2, ln2) == (S, ln)
                     tmax = max(tm, 1)
-                    assert ln % 64 == 0 and 64 <= ln <= 4096 and ln <= _rup(tmax, 64)
-                    assert 1 <= S <= 2048 and S * ln >= tmax and (S - 1) * ln < tmax
+                    assert ln % 64 == 0 and 64 <= ln <= 4096
+                    assert 1 <= S <= 2048 and S * ln >= tmax
+                    if streamed:
+                        # equal tile ranges over the pairs' tiles end to end: they cover
+                        # every tile, and a pair meets at most S of them
+                        assert not req and 0 < t_sum < 0.85 * batch * tmax and batch <= 256
+                        longest = ln // 64
+                        assert longest >= 4 and waves * longest >= H * (-(-t_sum // 64) + batch)
+                        assert -(-(-(-tmax // 64)) // longest) + 1 <= S <= -(-tmax // 64)
+                        need = batch * H * (S * ((D + 4) * 4 + 4) + _rup(tmax, 64) * 8)
+                    else:
+                        assert waves == 0 and (S - 1) * ln < tmax and ln <= _rup(tmax, 64)
+                        need = batch * H * S * ((D + 4) * 4 + 4 + ln * 8)
                     if req:   # more than requested only where splits would exceed 4096 tokens
                         assert S <= max(req, -(-tmax // 4096))
-                    need = batch * H * S * ((D + 4) * 4 + 4 + ln * 8)
                     assert p.decode_workspace_bytes(batch, tm) >= need, (batch, tm, t_sum, req, S, ln)
                     checked += 1
     assert checked > 500
