@@ -490,10 +490,15 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
   __syncthreads();
 
   // this head's pool region as a raw buffer: 32-bit offsets, and loads past
-  // the region return zero instead of faulting
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.pool + static_cast<int64_t>(h) * a.num_pages * L.HB), static_cast<short>(0),
-      static_cast<int>(static_cast<uint32_t>(a.num_pages * L.HB)), 0x00020000);
+  // the region return zero instead of faulting.  A region of no records
+  // turns the loads issued for a split's last tile (see the tile loop) into
+  // ones that return zeros without a memory request.
+  uint8_t* const region_base = const_cast<uint8_t*>(a.pool + static_cast<int64_t>(h) * a.num_pages * L.HB);
+  const int region_bytes = static_cast<int>(static_cast<uint32_t>(a.num_pages * L.HB));
+  auto region = [&](bool live) {
+    return __builtin_amdgcn_make_buffer_rsrc(region_base, static_cast<short>(0), live ? region_bytes : 0,
+                                             0x00020000);
+  };
   const int vj = lane % kNJ, vslot = lane / kNJ;
   const int gsel = lane >> 5;
   const int d0 = (lane & 31) * kCPL;
@@ -510,23 +515,24 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
   // The cache is streamed: every byte is read once per launch.  Loads carry
   // the non-temporal hint, which raises this chip's streaming-read rate by
   // about 12% (6.1 -> 6.9 TB/s on an 805 MB read).
-  auto ld128 = [&](uint32_t voff, uint32_t soff) -> uint4 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, kStreamLoad);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-  };
-  auto ld64 = [&](uint32_t voff, uint32_t soff) -> uint2 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, kStreamLoad);
-    return make_uint2(v[0], v[1]);
-  };
-  auto ld32 = [&](uint32_t voff, uint32_t soff) -> uint32_t {
-    return __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, soff, kStreamLoad);
-  };
-
-  // Issue every load of the tile starting at t0.  Rows past the split's end
-  // read whatever their (possibly unmapped) page offsets point to inside the
-  // head's region; the buffer bounds keep that safe and the results are
-  // masked out.
-  auto fetch = [&](Tile& td, int t0) {
+  // Issue every load of the tile starting at t0 (live: into the head's
+  // region; else the same instructions over an empty region).  Rows past
+  // the split's end read whatever their (possibly unmapped) page offsets
+  // point to inside the head's region; the buffer bounds keep that safe and
+  // the results are masked out.
+  auto fetch = [&](Tile& td, int t0, bool live) {
+    const auto rsrc = region(live);
+    auto ld128 = [&](uint32_t voff, uint32_t soff) -> uint4 {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, kStreamLoad);
+      return make_uint4(v[0], v[1], v[2], v[3]);
+    };
+    auto ld64 = [&](uint32_t voff, uint32_t soff) -> uint2 {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, kStreamLoad);
+      return make_uint2(v[0], v[1]);
+    };
+    auto ld32 = [&](uint32_t voff, uint32_t soff) -> uint32_t {
+      return __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, soff, kStreamLoad);
+    };
     const int tp0 = (t0 - start) >> lgP;
     {
       const uint32_t ro = pgoff[tp0 + lane_kpage] + lane_krow;
@@ -821,17 +827,18 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
   if (a.graded_priority) set_priority(3);
 
   // ping-pong over two tile buffers: the next tile's loads are issued before
-  // the current tile computes.  A tile with no successor re-issues its own
-  // loads (cache hits) so that every iteration has the same load pattern.
+  // the current tile computes.  A tile with no successor issues the same
+  // loads over an empty region (no memory traffic) so that every iteration
+  // has the same load pattern.
   Tile bufA, bufB;
-  fetch(bufA, start);
+  fetch(bufA, start, true);
   for (int t0 = start;;) {
-    fetch(bufB, t0 + kTile < end ? t0 + kTile : t0);
+    fetch(bufB, t0 + kTile < end ? t0 + kTile : t0, t0 + kTile < end);
     compute(bufA, t0);
     progress();
     t0 += kTile;
     if (t0 >= end) break;
-    fetch(bufA, t0 + kTile < end ? t0 + kTile : t0);
+    fetch(bufA, t0 + kTile < end ? t0 + kTile : t0, t0 + kTile < end);
     compute(bufB, t0);
     progress();
     t0 += kTile;

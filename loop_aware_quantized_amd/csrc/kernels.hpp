@@ -97,7 +97,7 @@ constexpr int kVqSplitMax = 32768;   // tokens per decode split
 
 struct VqArgs {
   uint8_t* pool;                     // [H][num_pages]: [P][D/4] key, then [P][D/4] value indices
-  const uint16_t* cb_k;              // [D/4][256][4R] fp16 codebook of the keys
+  const uint16_t* cb_k;              // [R][256][D/4][4] fp16 codebook of the keys (loop-major)
   const uint16_t* cb_v;              // same for the values
   const int32_t* seq_lens;
   const int32_t* block_tables;

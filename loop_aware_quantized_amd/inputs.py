@@ -68,6 +68,9 @@ WORKLOADS = {
     "ragged-16k": Workload("ragged-16k", 3, batch=64, loops=4, layers=24, heads=16,
                            head_dim=128, page=16, ctx=16384, ctx_min=512, shuffle_pages=True,
                            heavy_frac=0.005, plan="random", taus=(0.005,)),
+    # lean-16k's shape, plan and data over 16-token pages (two pages per key group)
+    "lean-16k-p16": Workload("lean-16k-p16", 2, batch=32, loops=4, layers=24, heads=16, head_dim=128,
+                             page=16, ctx=16384, plan="lean", taus=(0.01,), append_tokens=1),
     # KIVI-4-style baseline on the lean-16k shape and data: every cell stored
     # at 4 bits, no reuse, tau = 0 (every low plane read)
     "kivi4-16k": Workload("kivi4-16k", 2, batch=32, loops=4, layers=24, heads=16, head_dim=128,
