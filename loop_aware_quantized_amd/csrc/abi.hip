@@ -118,7 +118,7 @@ const char* batch_error(const loopkv_batch* b) {
 struct Splits {
   int S, len;
   bool streamed = false;
-  int tpw = 0, waves = 0;
+  int tpw = 0, waves = 0, main_waves = 0, tail_tiles = 1;
   int64_t cand_stride = 0;
 };
 
@@ -141,21 +141,41 @@ Splits uniform(int64_t tm, int64_t len) {
 // kMaxSplits; a requested count gives splits of ceil(t_max / count) tokens
 // rounded up to a tile.  No split exceeds kMaxSplitLen or the longest
 // sequence rounded up to a tile.
-// Streamed layout for a ragged batch: one round of waves (12 per compute
-// unit) with equal ranges of the pairs' tiles laid end to end, so that every
-// wave is busy for about the same time whatever the lengths.  Ranges hold
-// at least 4 tiles and at most a split's 4096 tokens (more waves than one
-// round otherwise).  Needs the length sum, at most kMaxStreamedBatch
-// sequences, and records per pair within the workspace's split capacity.
+// Streamed layout for a ragged batch.  The pairs' tiles are laid end to
+// end; one round of waves (12 per compute unit) takes equal ranges of the
+// first 90% of them, and a second round takes the rest in ranges of
+// kTailTiles tiles.  Waves of the first round finish spread over ~25% of
+// the launch (a SIMD issues its oldest wave first); the second round's
+// waves start in the slots that free up first, so the short ranges fill the
+// end of the launch instead of idle slots.  Short ranges also mean more
+// records and more candidates (each record's running threshold sees fewer
+// tokens) for the merge.  Measured on ragged-16k (64 x 16 pairs), whole
+// decode step: 16-tile ranges 2.5-3% faster than one round of equal
+// ranges; 8-tile ranges speed the split kernel 1% more but cost the merge
+// 0.3 ms; 5% or 15% tails gain less.  Ranges hold at least 4 tiles and at
+// most a split's 4096 tokens.  Needs the length sum, at most
+// kMaxStreamedBatch sequences, and records per pair within the workspace's
+// split capacity.
+constexpr double kTailShare = 0.10;
+constexpr int64_t kTailTiles = 16;
+
 bool streamed_layout(int64_t batch, int64_t heads, int64_t tm, int64_t t_sum, int64_t slots, Splits* out) {
   if (t_sum <= 0 || batch > lkv::kMaxStreamedBatch) return false;
   const int64_t tiles_ub = heads * ((t_sum + lkv::kTile - 1) / lkv::kTile + batch);   // >= the real count
   if (tiles_ub > (int64_t{1} << 30)) return false;
-  int64_t tpw = std::max<int64_t>(4, (tiles_ub + slots - 1) / slots);
+  const int64_t main_tiles = static_cast<int64_t>(static_cast<double>(tiles_ub) * (1.0 - kTailShare));
+  int64_t tpw = std::max<int64_t>(4, (main_tiles + slots - 1) / slots);
   tpw = std::min<int64_t>(tpw, lkv::kMaxSplitLen / lkv::kTile);
-  const int64_t waves = (tiles_ub + tpw - 1) / tpw;
+  const int64_t main_waves = std::min<int64_t>(slots, (tiles_ub + tpw - 1) / tpw);
+  const int64_t tail_tiles = std::min<int64_t>(kTailTiles, tpw);
+  const int64_t rest = std::max<int64_t>(0, tiles_ub - main_waves * tpw);
+  const int64_t waves = main_waves + (rest + tail_tiles - 1) / tail_tiles;
+  out->main_waves = static_cast<int>(main_waves);
+  out->tail_tiles = static_cast<int>(tail_tiles);
   const int64_t pair_tiles = (tm + lkv::kTile - 1) / lkv::kTile;
-  const int64_t recs = (pair_tiles + tpw - 1) / tpw + 1;   // a pair's tiles meet at most this many ranges
+  // A pair's n tiles meet at most ceil(n / tail) + 1 ranges (each range,
+  // also past the grid, has tail_tiles or more), whatever the hint.
+  const int64_t recs = (pair_tiles + tail_tiles - 1) / tail_tiles + 1;
   const int64_t s_cap = std::min<int64_t>(lkv::kMaxSplits, pair_tiles);
   if (recs > s_cap || waves > 0x7fffffff) return false;
   out->S = static_cast<int>(recs);
@@ -652,6 +672,8 @@ int decode_impl(const char* who, const loopkv_plan* plan, const loopkv_cell_mem*
   a.streamed = sp.streamed ? 1 : 0;
   a.tiles_per_wave = sp.tpw;
   a.waves = sp.waves;
+  a.main_waves = sp.main_waves;
+  a.tail_tiles = sp.tail_tiles;
   a.batch = batch->batch;
   a.cand_stride = static_cast<int32_t>(sp.cand_stride);
   const int64_t waves = sp.streamed ? sp.waves : static_cast<int64_t>(sp.S) * plan->H * batch->batch;

@@ -149,6 +149,24 @@ struct TileData {
   uint32_t ks[D / 64], kz[D / 64];  // key-group scale / zero of this lane's channels
 };
 
+__device__ __forceinline__ int range_start(const DecodeArgs& a, int w) {
+  return w < a.main_waves ? w * a.tiles_per_wave
+                          : a.main_waves * a.tiles_per_wave + (w - a.main_waves) * a.tail_tiles;
+}
+// Ranges continue past the grid with tail_tiles each (a length-sum hint
+// below the real sum leaves tiles there); the grid's last wave takes them
+// in turn, one record per range as for any other wave.
+__device__ __forceinline__ int wave_of(const DecodeArgs& a, int t) {
+  const int m = a.main_waves * a.tiles_per_wave;
+  return t < m ? t / a.tiles_per_wave : a.main_waves + (t - m) / a.tail_tiles;
+}
+// A sequence's length in the streamed layout, capped at the caller's
+// maximum (cand_stride is that maximum rounded up to a tile) so that a
+// length breaking the contract still reads and writes in bounds.
+__device__ __forceinline__ int streamed_len(const DecodeArgs& a, int b) {
+  return min(max(a.seq_lens[b], 0), a.cand_stride);
+}
+
 // One wave per (head, sequence): log-sum-exp merge of the S_used partials,
 // then (sparse mode) the exact test p_t >= tau over the candidate lists,
 // the mask bits and the low-plane correction of the flagged tokens.  The
@@ -189,12 +207,14 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   float2 ml_raw = make_float2(-INFINITY, 0.0f);
   if (lane < a.S) ml_raw = *reinterpret_cast<const float2*>(parts + lane * kRec);
   const int cnt_raw = (kSparse && lane < a.S) ? a.cand_count[pair * a.S + lane] : 0;
+  // records requested before the length arrives
+  const int n_first = min(kFirst, a.S);
   float v0[kFirst][kCPL];
 #pragma unroll
   for (int u = 0; u < kFirst; ++u) {
     const float* rec = parts + (u < a.S ? u : 0) * kRec + kPartialPad;
 #pragma unroll
-    for (int c = 0; c < kCPL; ++c) v0[u][c] = rec[lane + 64 * c];
+    for (int c = 0; c < kCPL; ++c) v0[u][c] = u < n_first ? rec[lane + 64 * c] : 0.0f;
   }
   // streamed layout: tiles (all heads) of the sequences before this one
   int tiles_before = 0;
@@ -202,10 +222,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < kMaxStreamedBatch / 64; ++k) {
       const int bb = lane + 64 * k;
-      tiles_before += bb < b ? a.H * ((max(a.seq_lens[bb], 0) + kTile - 1) / kTile) : 0;
+      tiles_before += bb < b ? a.H * ((streamed_len(a, bb) + kTile - 1) / kTile) : 0;
     }
   }
-  const int T = a.seq_lens[b];
+  const int T = a.streamed ? streamed_len(a, b) : a.seq_lens[b];
   uint32_t* mrow = a.mask_bits ? a.mask_bits + pair * a.mask_words : nullptr;
   if (T <= 0) {
     for (int d = lane; d < D; d += 64) outp[d] = 0.0f;
@@ -216,21 +236,21 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   }
   // Records of the pair and the first token of each.  Uniform: record r is
   // split r.  Streamed: the pair's tiles start at tile0 of the end-to-end
-  // order, and record r is the part of wave (tile0 / tpw + r)'s range in it.
-  const int tpw = a.tiles_per_wave;
-  int tile0 = 0, S_used;
+  // order, and record r is the part of range (wave_of(tile0) + r) in it.
+  int tile0 = 0, w0 = 0, S_used;
   if (a.streamed) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) tiles_before += __shfl_xor(tiles_before, o, 64);
     const int nb = (T + kTile - 1) / kTile;
     tile0 = tiles_before + h * nb;
-    S_used = min((tile0 + nb - 1) / tpw - tile0 / tpw + 1, a.S);
+    w0 = wave_of(a, tile0);
+    S_used = min(wave_of(a, tile0 + nb - 1) - w0 + 1, a.S);
   } else {
     // lengths above max_seq_len break the caller's contract; never read past S
     S_used = min((T + a.split_len - 1) / a.split_len, a.S);
   }
   auto rec_start = [&](int r) -> int {
-    return a.streamed ? max(0, (tile0 / tpw + r) * tpw - tile0) * kTile : r * a.split_len;
+    return a.streamed ? max(0, range_start(a, w0 + r) - tile0) * kTile : r * a.split_len;
   };
   // the row was cleared by the split kernel (the split holding token 0)
   const float m_l = lane < S_used ? ml_raw.x : -INFINITY;
@@ -253,22 +273,23 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     for (int u = 0; u < kFirst; ++u) {
       const float e = lane_f(e0, u);
 #pragma unroll
-      for (int c = 0; c < kCPL; ++c) o[c] = u < S_used ? fmaf(e, v0[u][c], o[c]) : o[c];   // stale past S_used
+      for (int c = 0; c < kCPL; ++c)
+        o[c] = u < S_used && u < n_first ? fmaf(e, v0[u][c], o[c]) : o[c];   // stale past S_used
     }
     for (int i0 = 0; i0 < S_used; i0 += 64) {
       const int n = min(64, S_used - i0);
       const float e_l = i0 == 0 ? e0 : (lane < n ? __expf(parts[(i0 + lane) * kRec] - M) : 0.0f);
-      // eight records per step, all loads issued before the first use
-      for (int j = i0 == 0 ? kFirst : 0; j < n; j += 8) {
-        float v[8][kCPL];
+      // sixteen records per step, all loads issued before the first use
+      for (int j = i0 == 0 ? n_first : 0; j < n; j += 16) {
+        float v[16][kCPL];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const float* rec = parts + (i0 + j + u) * kRec + kPartialPad;
 #pragma unroll
           for (int c = 0; c < kCPL; ++c) v[u][c] = (j + u < n) ? rec[lane + 64 * c] : 0.0f;
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const float e = lane_f(e_l, (j + u) & 63);   // 0 past n
 #pragma unroll
           for (int c = 0; c < kCPL; ++c) o[c] = fmaf(e, v[u][c], o[c]);
@@ -882,43 +903,44 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 }
 
 // Streamed layout: wave w takes its range of the pairs' tiles laid end to
-// end (sequence-major, then head), one split segment per pair it meets.  The tile counts of all sequences (B <= 256)
-// are scanned once into LDS.
+// end (sequence-major, then head), one split segment per pair it meets.
+// The tile counts of all sequences (B <= 256) are scanned once into LDS.
 template <int D, int KIND, int MODE>
 __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs a) {
   __shared__ int seq_first[kMaxStreamedBatch + 1];   // first tile of each sequence, then the total
   const int lane = threadIdx.x;
   const int H = a.H;
-  int tl[4];
-  int own = 0;
+  int own[4], sum = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int bb = 4 * lane + k;
-    const int T = bb < a.batch ? max(a.seq_lens[bb], 0) : 0;
-    tl[k] = H * ((T + kTile - 1) / kTile);   // tiles of all heads of sequence bb
-    own += tl[k];
+    own[k] = bb < a.batch ? H * ((streamed_len(a, bb) + kTile - 1) / kTile) : 0;
+    sum += own[k];
   }
-  int incl = own;
+  int incl = sum;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(incl, o, 64);
     if (lane >= o) incl += y;
   }
-  int run = incl - own;
+  int run = incl - sum;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     seq_first[4 * lane + k] = run;
-    run += tl[k];
+    run += own[k];
   }
   if (lane == 63) seq_first[kMaxStreamedBatch] = run;
   __syncthreads();
-  const int total = seq_first[kMaxStreamedBatch];
-  const int tpw = a.tiles_per_wave;
-  const int w = blockIdx.x;
-  int t = w * tpw;
-  const int t_end = min(t + tpw, total);
-  while (t < t_end) {
-    // the sequence holding tile t: the last b < B with seq_first[b] <= t
+  // Wave w takes range w; the last wave then the ranges past the grid.  Only
+  // t is carried across segments; the rest is read again from LDS and the
+  // arguments (fewer scalars live across the segment's body).
+  int t = range_start(a, blockIdx.x);
+  while (true) {
+    const int total = seq_first[kMaxStreamedBatch];
+    const int w = blockIdx.x;
+    const int t_end = w == a.waves - 1 ? total : min(range_start(a, w + 1), total);
+    if (t >= t_end) break;
+    // the sequence holding tile t: the last b < B whose first tile is <= t
     int lo = 0, hi = a.batch - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -926,15 +948,16 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs a) {
       else hi = mid - 1;
     }
     const int b = __builtin_amdgcn_readfirstlane(lo);
-    const int first_tile = __builtin_amdgcn_readfirstlane(seq_first[b]);
-    const int T = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
-    const int nb = (T + kTile - 1) / kTile;              // tiles per head
-    const int h = (t - first_tile) / nb;
-    const int j = t - first_tile - h * nb;               // tile index within the pair
-    const int seg = min(nb - j, t_end - t);
-    const int pair_first = first_tile + h * nb;
-    split_segment<D, KIND, MODE>(a, b, h, T, j * kTile, min((j + seg) * kTile, T), w - pair_first / tpw, j == 0);
-    __syncthreads();                                     // LDS of this segment is free again
+    const int first = __builtin_amdgcn_readfirstlane(seq_first[b]);
+    const int T = __builtin_amdgcn_readfirstlane(streamed_len(a, b));
+    const int nb = (T + kTile - 1) / kTile;                // tiles per head
+    const int h = (t - first) / nb;
+    const int j = t - first - h * nb;                      // tile index within the pair
+    const int wv = wave_of(a, t);                          // w, or a range past the grid
+    const int seg = min(nb - j, min(range_start(a, wv + 1), t_end) - t);
+    const int rec = wv - wave_of(a, first + h * nb);       // record number within the pair
+    split_segment<D, KIND, MODE>(a, b, h, T, j * kTile, min((j + seg) * kTile, T), rec, j == 0);
+    __syncthreads();                                       // LDS of this segment is free again
     t += seg;
   }
 }

@@ -49,13 +49,16 @@ struct DecodeArgs {
   // Split layout.  Uniform (streamed == 0): the grid is (S, H, B) and split
   // k of a (sequence, head) covers tokens [k * split_len, (k + 1) *
   // split_len).  Streamed: the (sequence, head) pairs' 64-token tiles are
-  // laid end to end (sequence-major, then head) and wave w of a 1-D grid
-  // takes tiles [w * tiles_per_wave, (w + 1) * tiles_per_wave); each pair it
-  // touches gets one partial record, numbered from the first wave that
-  // touches the pair.  S: partial records per pair; cand_stride: candidate
-  // entries per pair (a record's list starts at its first token's offset).
+  // laid end to end (sequence-major, then head) and cut into consecutive
+  // ranges: tiles_per_wave tiles for ranges below main_waves, tail_tiles
+  // after.  Wave w of the 1-D grid (waves waves) takes range w, the last
+  // wave also the ranges past the grid; each pair gets one partial record
+  // per range that meets it.  S: partial records per pair; cand_stride:
+  // candidate entries per pair (a record's list starts at its first token's
+  // offset), also the cap on a length.
   int32_t streamed;
   int32_t tiles_per_wave;
+  int32_t main_waves, tail_tiles;
   int32_t waves;                     // streamed: the grid
   int32_t batch;
   int32_t cand_stride;

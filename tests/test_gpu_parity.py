@@ -338,6 +338,32 @@ def test_many_short_ragged_pairs():
         assert torch.isfinite(out).all()
 
 
+@pytest.mark.parametrize("hint_scale", [1.0, 0.5, 0.05, 1.45])
+def test_streamed_layout_any_length_hint(hint_scale):
+    """A ragged batch in the streamed split layout, with the length-sum hint
+    exact, too small (tiles past the ranges go to the last wave) and too
+    large: every sampled sequence matches the oracle."""
+    B, H = 24, 8
+    lens = np.random.default_rng(77).integers(100, 6000, B).astype(np.int64)
+    lens[3] = 6000
+    w = wl.Workload("hint", 195, batch=B, loops=1, layers=2, heads=H, head_dim=128, page=32,
+                    ctx=6000, heavy_frac=0.01)
+    st = runner.CacheState(w, DEV, [[Q4, Q2]], [[0.01, math.inf]], lengths=list(lens))
+    seqs = [0, 3, B - 1]
+    kept = st.prefill({c: set(seqs) for c in st.stored})
+    hint = max(1, int(lens.sum() * hint_scale))
+    streamed, S, ln, waves = abi.loopkv_decode_layout(st.plan, 0, 0, B, 6000, hint, 0)
+    assert streamed, "a ragged batch with a length hint takes the streamed layout"
+    for l in range(2):
+        q = wl.cell_query(w, st.cell_index(0, l), DEV)[1]
+        out = torch.empty(B, H, w.head_dim, dtype=torch.float32, device=DEV)
+        mask = st.new_mask()
+        st.decode(0, l, q, out, mask=mask, sum_seq_lens=hint)
+        torch.cuda.synchronize()
+        s = compare_decode(st, 0, l, q, out, mask, kept[(0, l)], seqs)
+        say(f"  hint x{hint_scale} layer {l}: {waves} waves, {S} records per pair, rel err {s['rel']:.2e}")
+
+
 def test_graph_replay_matches_eager():
     """Appends and decodes captured in one HIP graph give, on every replay,
     the same bytes as the same calls made eagerly (eager work and
