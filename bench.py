@@ -42,7 +42,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-samples", type=int, default=0,
                     help="oracle samples: (cell, sequence) decodes, or (layer, loop, sequence) for the joint-code "
-                         "workloads; 0 = about 10 s of single-core work (16, or 40 for joint codes)")
+                         "workloads; 0 = 64 (about 35 s of single-core work over the workers), or 40 for joint codes")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="oracle worker processes (capped by the host's cores); 16 is one GPU's share of a box")
+    ap.add_argument("--extra", default="ragged-16k,lean-16k-p16",
+                    help="comma-separated workloads also timed (no oracle) and reported under 'extra'")
     ap.add_argument("--report", default=None, help="also write the JSON result to this file")
     ap.add_argument("--planner", action="store_true",
                     help="only time the offline plan search (host) and exit")
@@ -339,15 +343,49 @@ def recorded_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch_avg")
 
 
-def cpu_baseline(w, st, kinds, taus, n_samples, dev):
-    """Time oracle.attention.decode on (cell, sequence) samples (cache build excluded)."""
+def _oracle_worker(job):
+    """Worker process of the CPU baseline: build the oracle caches of its
+    samples (not timed), wait for every worker, then time the decodes
+    single-threaded.  Returns (start, end, per-sample seconds, tokens)."""
     import oracle.attention as oa
     import oracle.cache as oc
-    from loop_aware_quantized_amd import inputs as wl
+    samples, barrier = job["samples"], _BARRIER
     try:
         from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1)
     except ImportError:  # pragma: no cover
-        threadpool_limits = None
+        limit = None
+    caches = [oc.build_cell_cache(s["kb"], s["vb"], s["kind"]) for s in samples]
+    barrier.wait()
+    t0 = time.time()
+    per = []
+    for s, c in zip(samples, caches):
+        a = time.perf_counter()
+        oa.decode(c, s["qb"], s["tau"])
+        per.append(time.perf_counter() - a)
+    t1 = time.time()
+    del limit
+    return t0, t1, per, sum(s["T"] for s in samples)
+
+
+_BARRIER = None
+
+
+def _init_worker(barrier):
+    global _BARRIER
+    _BARRIER = barrier
+
+
+def cpu_baseline(w, st, kinds, taus, n_samples, dev, workers):
+    """Time oracle.attention.decode on (cell, sequence) samples on the host
+    cores: `workers` single-threaded processes run at once (cache build
+    excluded); the rate is the samples' tokens over the wall time from the
+    first worker's start to the last one's end."""
+    import multiprocessing as mp
+    import os
+    from concurrent.futures import ProcessPoolExecutor
+    import oracle.attention as oa
+    from loop_aware_quantized_amd import inputs as wl
     R, L = w.loops, w.layers
     rng = np.random.default_rng(12345)
     # cover 4-bit, 2-bit, reuse->4-bit and reuse->2-bit cells
@@ -360,31 +398,32 @@ def cpu_baseline(w, st, kinds, taus, n_samples, dev):
     keys = sorted(groups)
     picks = [groups[keys[i % len(keys)]][rng.integers(len(groups[keys[i % len(keys)]]))]
              for i in range(n_samples)]
-    t_total, tokens = 0.0, 0
+    samples = []
     for (r, l) in picks:
         sr, sl = oa.resolve_source(kinds, r, l)
         b = int(rng.integers(w.batch))
         T = int(st.lens0[b])
         K, V = wl.cell_kv(w, st.cell_index(sr, sl), T, dev, b, b + 1)
-        kb, vb = wl.bf16_bits(K[0]), wl.bf16_bits(V[0])
+        samples.append({"kb": wl.bf16_bits(K[0]), "vb": wl.bf16_bits(V[0]), "kind": int(kinds[sr, sl]),
+                        "qb": wl.bf16_bits(wl.cell_query(w, st.cell_index(r, l), dev)[1])[b],
+                        "tau": float(taus[r, l]), "T": T})
         del K, V
-        cache = oc.build_cell_cache(kb, vb, int(kinds[sr, sl]))
-        qb = wl.bf16_bits(wl.cell_query(w, st.cell_index(r, l), dev)[1])[b]
-        if threadpool_limits is not None:
-            with threadpool_limits(limits=1):
-                t0 = time.perf_counter()
-                oa.decode(cache, qb, float(taus[r, l]))
-                t_total += time.perf_counter() - t0
-        else:
-            t0 = time.perf_counter()
-            oa.decode(cache, qb, float(taus[r, l]))
-            t_total += time.perf_counter() - t0
-        tokens += T
-        log(f"[bench] oracle sample cell ({r},{l}) seq {b}: T={T} cumulative {t_total:.1f} s")
-    return {"value": tokens / t_total, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(picks)} (cell, sequence) decodes of {w.name}, all {w.heads} heads, "
-                      f"{tokens} KV tokens, cache build excluded, numpy single thread",
-            "seconds": t_total}
+    workers = max(1, min(workers, os.cpu_count() or 1, len(samples)))
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(workers)
+    jobs = [{"samples": samples[i::workers]} for i in range(workers)]
+    log(f"[bench] oracle baseline: {len(samples)} (cell, sequence) decodes on {workers} worker processes")
+    with ProcessPoolExecutor(workers, mp_context=ctx, initializer=_init_worker, initargs=(barrier,)) as ex:
+        res = list(ex.map(_oracle_worker, jobs))
+    wall = max(r[1] for r in res) - min(r[0] for r in res)
+    per = [x for r in res for x in r[2]]
+    tokens = sum(r[3] for r in res)
+    log(f"[bench] oracle baseline: {tokens} KV tokens in {wall:.1f} s wall, {sum(per):.1f} s of decode work")
+    return {"value": tokens / wall, "unit": "KV tokens/s", "cores": workers, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(),
+            "sample": f"{len(samples)} (cell, sequence) decodes of {w.name}, all {w.heads} heads, {tokens} KV "
+                      f"tokens, cache build excluded; {workers} single-threaded worker processes at once",
+            "seconds": wall, "single_core_value": tokens / sum(per)}
 
 
 def vq_main(args, w):
@@ -582,7 +621,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, bench.st, kinds, bench.taus, args.cpu_samples or 16, bench.dev)
+        cpu = cpu_baseline(w, bench.st, kinds, bench.taus, args.cpu_samples or 64, bench.dev, args.cpu_workers)
 
     st = bench.st
     q4_cells = [c for c in st.stored if kinds[c] == wl.KIND_Q4]
@@ -590,6 +629,25 @@ def main():
     all_q4_bytes = (w.loops * w.layers * st.plan.pool_bytes(*q4_cells[0], st.num_pages)
                     if q4_cells else None)
     sp = primary["split"]
+    del bench, st
+    torch.cuda.empty_cache()
+    extra = {}
+    for name in [x for x in args.extra.split(",") if x and x != w.name]:
+        ew = wl.WORKLOADS[name]
+        ek, et = wl.make_plan(ew)
+        eb = Bench(args, ew, ek, et, 1)
+        r = eb.run_point()
+        esp = r["split"]
+        extra[name] = {"ms_per_step": r["ms_per_step"], "kv_tokens_per_s": r["value"],
+                       "hbm_gbs_required": r["hbm_gbs_required"], "page": ew.page, "batch": ew.batch,
+                       "context": r["context"],
+                       "split_roofline": {"achieved": esp["achieved_gbs"], "frac": esp["achieved_gbs"] / HBM_PEAK_GBS,
+                                          "avg_launch_us": esp["ms"] * 1e3 / max(esp["launches"], 1),
+                                          "launches": esp["launches"]},
+                       "kernels_ms_per_step": r["kernels_ms_per_step"], "lo_plane": r["lo_plane"]}
+        log(f"[bench] extra {name}: {r['ms_per_step']:.3f} ms/step, split {esp['achieved_gbs']:.0f} GB/s")
+        del eb
+        torch.cuda.empty_cache()
     res = {
         "metric": METRIC,
         "value": primary["value"],
@@ -625,6 +683,7 @@ def main():
         "storage": {"stored_bytes": stored_bytes, "all_4bit_bytes": all_q4_bytes,
                     "saving_vs_all_4bit": (1 - stored_bytes / all_q4_bytes) if all_q4_bytes else None},
         "cpu_baseline": cpu,
+        "extra": extra,
     }
     if args.tau_sweep:
         res["tau_sweep"] = [{"tau": p["tau"], "ms_per_step": p["ms_per_step"],
