@@ -629,6 +629,12 @@ def main():
     all_q4_bytes = (w.loops * w.layers * st.plan.pool_bytes(*q4_cells[0], st.num_pages)
                     if q4_cells else None)
     sp = primary["split"]
+    # the split pass's kernel: the streamed variant where the cell's layout is streamed
+    hint = int(bench.lens_of(0).sum())
+    streamed = {bool(bench.abi.loopkv_decode_layout(st.plan, r, l, w.batch, st.max_seq_len, hint,
+                                                     args.num_splits)[0]) for (r, l) in bench.order}
+    split_kernel = "+".join(k for k, on in (("decode_split_kernel", False in streamed),
+                                            ("decode_stream_kernel", True in streamed)) if on)
     del bench, st
     torch.cuda.empty_cache()
     extra = {}
@@ -668,7 +674,7 @@ def main():
                    "step_launch": "hip_graph" if args.graph else "eager"},
         "hbm_gbs_required": primary["hbm_gbs_required"],
         "hbm_frac_required": primary["hbm_gbs_required"] / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": sp["achieved_gbs"],
+        "roofline": {"bound": "hbm", "kernel": split_kernel, "achieved": sp["achieved_gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": sp["achieved_gbs"] / HBM_PEAK_GBS,
                      "traffic": recorded_traffic(w.name), "traffic_unit": "bytes per launch",
                      "launches": sp["launches"],
