@@ -351,8 +351,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     };
 
     // The lists of up to 64 splits are scanned as one flat sequence, kPass
-    // entries per lane per pass: entry k finds its split by binary search
-    // over the inclusive prefix of the list lengths.
+    // entries per lane per pass: entry k finds its split by a branch-free
+    // binary search over the inclusive prefix of the list lengths (six LDS
+    // steps, the kPass searches interleaved).
     for (int i0 = 0; i0 < S_used; i0 += 64) {
       const int ns = min(64, S_used - i0);
       const int cnt = i0 == 0 ? cnt0 : (lane < ns ? a.cand_count[pair * a.S + i0 + lane] : 0);
@@ -371,20 +372,27 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
           flagged += nf;
           nf = 0;
         }
+        // split of entry k: the number of lists that end at or before k
+        // (pre[] of lanes past ns holds the total, which exceeds any k)
+        int sp[kPass];
+#pragma unroll
+        for (int u = 0; u < kPass; ++u) sp[u] = 0;
+#pragma unroll
+        for (int step = 32; step > 0; step >>= 1) {
+#pragma unroll
+          for (int u = 0; u < kPass; ++u) {
+            const int k = base + 64 * u + lane;
+            sp[u] += pre[sp[u] + step - 1] <= k ? step : 0;
+          }
+        }
         int2 c[kPass];
 #pragma unroll
         for (int u = 0; u < kPass; ++u) {
           const int k = base + 64 * u + lane;
           c[u] = make_int2(0, 0);
           if (k < total) {
-            int lo = 0, hi = ns - 1;
-            while (lo < hi) {
-              const int mid = (lo + hi) >> 1;
-              if (pre[mid] > k) hi = mid;
-              else lo = mid + 1;
-            }
-            const int before = lo ? pre[lo - 1] : 0;
-            c[u] = a.cand[pair * a.cand_stride + rec_start(i0 + lo) + (k - before)];
+            const int before = sp[u] ? pre[sp[u] - 1] : 0;
+            c[u] = a.cand[pair * a.cand_stride + rec_start(i0 + sp[u]) + (k - before)];
           }
         }
 #pragma unroll
