@@ -498,6 +498,7 @@ def vq_main(args, w):
         "metric": METRIC, "value": tokens * R * L / (ms / 1e3), "unit": "KV tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "arithmetic": "1-byte joint codes; fp16 codewords widened to f32; scores, softmax and accumulation in f32",
         "data": "synthetic (seeded loop-redundant bf16 K/V, synthetic codebooks)",
         "config": {"workload": w.name, "batch": B, "loops": R, "layers": L, "heads": H, "head_dim": D,
                    "page": w.page, "context": int(lens_of(first).max()), "bits_per_element": 8 / (4 * R),
@@ -666,6 +667,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "arithmetic": ("2/4-bit codes; scores and softmax in f32; value weights rounded to f16 (kept in its "
+                       "normal range) in f32-accumulated dot products"),
         "data": "synthetic (seeded N(0,1) bf16 K/V with outlier channels and heavy tokens)",
         "config": {"workload": w.name, "batch": w.batch, "loops": w.loops, "layers": w.layers,
                    "heads": w.heads, "head_dim": w.head_dim, "page": w.page,
