@@ -415,12 +415,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     gather(nf);
     flagged += nf;
 
+    // sum the token slots of each channel group (lanes of equal lane % kNJ)
 #pragma unroll
-    for (int o = kNJ; o < 64; o <<= 1) {
-#pragma unroll
-      for (int c = 0; c < 32; ++c) corr[c] += __shfl_xor(corr[c], o, 64);
-      cs += __shfl_xor(cs, o, 64);
-    }
+    for (int c = 0; c < 32; ++c) corr[c] = strided_sum<kNJ>(corr[c]);
+    cs = strided_sum<kNJ>(cs);
     if (lane < kNJ) {
 #pragma unroll
       for (int c = 0; c < 32; ++c) o_s[kGroup * lane + c] += corr[c] - 1.5f * cs;
@@ -876,11 +874,8 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
 
   // --- partial: sum the token slots of each channel group
 #pragma unroll
-  for (int o = kNJ; o < 64; o <<= 1) {
-#pragma unroll
-    for (int c = 0; c < 32; ++c) acc[c] += __shfl_xor(acc[c], o, 64);
-    zs += __shfl_xor(zs, o, 64);
-  }
+  for (int c = 0; c < 32; ++c) acc[c] = strided_sum<kNJ>(acc[c]);
+  zs = strided_sum<kNJ>(zs);
   lsum = dpp_wave_sum(lsum);
   if (lane < kNJ) {
 #pragma unroll

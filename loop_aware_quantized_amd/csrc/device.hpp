@@ -96,6 +96,25 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
 }
 
+// Sum over the lanes l' with l' = l (mod kStride), kStride in {1, 2, 4, 8}:
+// DPP row rotations within each 16-lane row (VALU), then the gfx950 lane
+// swaps across rows (the sum of a swap's two results is v[l] + v[l ^ 16],
+// resp. v[l] + v[l ^ 32], in every lane).  No LDS round trips.
+template <int kStride>
+__device__ __forceinline__ float strided_sum(float v) {
+  static_assert(kStride == 1 || kStride == 2 || kStride == 4 || kStride == 8, "stride");
+  if (kStride <= 1) v += dpp_f<0x121>(v);    // row_ror:1
+  if (kStride <= 2) v += dpp_f<0x122>(v);    // row_ror:2
+  if (kStride <= 4) v += dpp_f<0x124>(v);    // row_ror:4
+  v += dpp_f<0x128>(v);                      // row_ror:8
+  const uint32_t u = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const uint32_t w = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 // every lane of each 16-lane row receives the row's sum / max
 __device__ __forceinline__ float row_sum(float v) {
   v += dpp_f<0xB1>(v);
