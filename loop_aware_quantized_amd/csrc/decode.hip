@@ -258,11 +258,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int cnt0 = lane < S_used ? cnt_raw : 0;
   float M = m_l;
   for (int i = lane + 64; i < S_used; i += 64) M = fmaxf(M, parts[i * kRec]);
-  M = wave_max(M);
+  M = dpp_wave_max(M);
   const float e0 = lane < S_used ? __expf(m_l - M) : 0.0f;   // weight of split `lane`
   float lsum = e0 * l_l;
   for (int i = lane + 64; i < S_used; i += 64) lsum = fmaf(__expf(parts[i * kRec] - M), parts[i * kRec + 1], lsum);
-  lsum = wave_sum(lsum);
+  lsum = dpp_wave_sum(lsum);
   const float inv = 1.0f / lsum;
   const float lse = M + logf(lsum);
   {
@@ -357,13 +357,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     for (int i0 = 0; i0 < S_used; i0 += 64) {
       const int ns = min(64, S_used - i0);
       const int cnt = i0 == 0 ? cnt0 : (lane < ns ? a.cand_count[pair * a.S + i0 + lane] : 0);
-      int incl = cnt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-      }
-      const int total = __shfl(incl, 63, 64);
+      const int incl = wave_incl_scan(cnt);
+      const int total = __builtin_amdgcn_readlane(incl, 63);
       pre[lane] = incl;
       __syncthreads();
       for (int base = 0; base < total; base += 64 * kPass) {
@@ -920,12 +915,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs a) {
     own[k] = bb < a.batch ? H * ((streamed_len(a, bb) + kTile - 1) / kTile) : 0;
     sum += own[k];
   }
-  int incl = sum;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  const int incl = wave_incl_scan(sum);
   int run = incl - sum;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {

@@ -115,6 +115,24 @@ __device__ __forceinline__ float strided_sum(float v) {
   return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele within
+// each 16-lane row (DPP row_shr, lanes without a source add 0), then row
+// 15's total into rows 1 and 3 (row_bcast:15) and lane 31's into rows 2
+// and 3 (row_bcast:31).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xF, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i<0x111, 0xF>(v);   // row_shr:1
+  v += dpp_i<0x112, 0xF>(v);   // row_shr:2
+  v += dpp_i<0x114, 0xF>(v);   // row_shr:4
+  v += dpp_i<0x118, 0xF>(v);   // row_shr:8
+  v += dpp_i<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+  v += dpp_i<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // every lane of each 16-lane row receives the row's sum / max
 __device__ __forceinline__ float row_sum(float v) {
   v += dpp_f<0xB1>(v);
