@@ -148,13 +148,16 @@ int loopkv_decode_splits(const loopkv_plan* plan, int32_t batch, int32_t max_seq
 /* The split layout loopkv_decode uses for cell (loop, layer) and these host
  * fields: out[0] = 0 for a uniform layout (every (sequence, head) cut into
  * out[1] splits of out[2] tokens, as loopkv_decode_splits reports) or 1 for
- * a streamed one (out[3] waves, each taking an equal range of out[2] / 64
- * of the pairs' 64-token tiles laid end to end, sequence-major; a pair gets
- * one partial record per wave whose range meets it, at most out[1]).
+ * a streamed one: the pairs' 64-token tiles laid end to end (sequence-major,
+ * then head) and cut into ranges, the first ranges (about 90% of the tiles
+ * by the length-sum hint, one per resident wave slot) of out[2] / 64 tiles,
+ * the rest of 16; out[3] waves take one range each, and ranges past the
+ * grid (a hint below the real sum leaves some) go to the last wave in turn.
+ * A pair gets one partial record per range that meets it, at most out[1].
  * Streamed layouts serve ragged batches (a length sum below 85% of
  * batch * max_seq_len) of at most 256 sequences with a tau mask or none
- * (not tau = 0); every wave is then busy for the same time.  Errors:
- * LOOPKV_E_INVAL as loopkv_decode_splits, or a bad cell. */
+ * (not tau = 0).  Errors: LOOPKV_E_INVAL as loopkv_decode_splits, or a bad
+ * cell. */
 int loopkv_decode_layout(const loopkv_plan* plan, int loop, int layer, int32_t batch, int32_t max_seq_len,
                          int32_t sum_seq_lens, int32_t num_splits, int32_t out[4]);
 

@@ -162,7 +162,10 @@ constexpr int64_t kTailTiles = 16;
 bool streamed_layout(int64_t batch, int64_t heads, int64_t tm, int64_t t_sum, int64_t slots, Splits* out) {
   if (t_sum <= 0 || batch > lkv::kMaxStreamedBatch) return false;
   const int64_t tiles_ub = heads * ((t_sum + lkv::kTile - 1) / lkv::kTile + batch);   // >= the real count
-  if (tiles_ub > (int64_t{1} << 30)) return false;
+  // the kernels index tiles in 32 bits: bound the count by the lengths'
+  // maximum too, since the sum is only a hint
+  const int64_t tiles_max = heads * batch * ((tm + lkv::kTile - 1) / lkv::kTile);
+  if (tiles_ub > (int64_t{1} << 30) || tiles_max > (int64_t{1} << 30)) return false;
   const int64_t main_tiles = static_cast<int64_t>(static_cast<double>(tiles_ub) * (1.0 - kTailShare));
   int64_t tpw = std::max<int64_t>(4, (main_tiles + slots - 1) / slots);
   tpw = std::min<int64_t>(tpw, lkv::kMaxSplitLen / lkv::kTile);
