@@ -364,18 +364,25 @@ def test_streamed_layout_any_length_hint(hint_scale):
         say(f"  hint x{hint_scale} layer {l}: {waves} waves, {S} records per pair, rel err {s['rel']:.2e}")
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("ragged", [False, True])
+def test_graph_replay_matches_eager(ragged):
     """Appends and decodes captured in one HIP graph give, on every replay,
     the same bytes as the same calls made eagerly (eager work and
     synchronizations run between the replays), and every replay's outputs
     and masks match the oracle on the sequence as it stands after that
-    replay's append."""
+    replay's append.  Ragged: the calls carry a length-sum hint of half the
+    real sum, so the streamed layout fixed at capture leaves tiles past its
+    grid (taken by the last wave), more of them on every replay."""
     w = wl.Workload("graph", 180, batch=3, loops=2, layers=2, heads=4, head_dim=128, page=16,
                     ctx=700, heavy_frac=0.01)
     kinds, taus = [[Q4, Q2], [Q4, Q4]], [[0.01, 0.01], [0.0, math.inf]]
     n_steps = 4
-    st_e = runner.CacheState(w, DEV, kinds, taus, extra_tokens=n_steps)
-    st_g = runner.CacheState(w, DEV, kinds, taus, extra_tokens=n_steps)
+    lengths = [700, 120, 333] if ragged else None
+    st_e = runner.CacheState(w, DEV, kinds, taus, extra_tokens=n_steps, lengths=lengths)
+    st_g = runner.CacheState(w, DEV, kinds, taus, extra_tokens=n_steps, lengths=lengths)
+    hint = int(st_e.lens0.sum()) // 2 if ragged else 0
+    if ragged:
+        assert abi.loopkv_decode_layout(st_e.plan, 0, 0, w.batch, st_e.max_seq_len, hint, 0)[0] == 1
     kept = None
     for st in (st_e, st_g):
         for c in st.stored:
@@ -392,7 +399,7 @@ def test_graph_replay_matches_eager():
         for c in st.stored:
             abi.loopkv_append(st.plan, st.cells, c[0], c[1], app, 1, *new[c])
         for i, (r, l) in enumerate(cells):
-            st.decode(r, l, qs[(r, l)], outs[i], mask=masks[i], lens=lens_dec, sum_seq_lens=0)
+            st.decode(r, l, qs[(r, l)], outs[i], mask=masks[i], lens=lens_dec, sum_seq_lens=hint)
 
     def buffers(st):
         return ([torch.empty(w.batch, w.heads, w.head_dim, dtype=torch.float32, device=DEV) for _ in cells],
