@@ -497,7 +497,12 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
       mrow[w] = bits;
     }
   }
-  if (start >= end) return;   // splits past the end take no part in the merge
+  if (start >= end) {         // splits past the end take no part in the merge
+    // one split per pair and no merge launch: the empty pair's output is zero
+    if (!kSparse && a.direct_out && rec == 0)
+      for (int d = lane; d < D; d += 64) a.out[pair * D + d] = 0.0f;
+    return;
+  }
 
   {
     const int np = ((end - start) + pmask) >> lgP;   // <= span: end <= T <= max_pages * P
@@ -872,6 +877,23 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
   for (int c = 0; c < 32; ++c) acc[c] = strided_sum<kNJ>(acc[c]);
   zs = strided_sum<kNJ>(zs);
   lsum = dpp_wave_sum(lsum);
+  if (!kSparse && a.direct_out) {
+    // The only split of its pair (no tau test to follow): the merge of one
+    // record is o / sum, written here, and no merge kernel runs.
+    const float inv = 1.0f / lsum;
+    if (lane < kNJ) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        a.out[pair * D + kGroup * lane + 16 * (c / 16) + pos_channel(c % 16)] =
+            fmaf(acc[c], kValComb ? inv_unit : dot2_factor(c % 16) * (kQ4 ? 4.0f : 1.0f), zs) * inv;
+    }
+    if (kDense && a.counters && lane == 0) {   // every low-plane row was read
+      const unsigned long long n = static_cast<unsigned long long>(end - start);
+      atomicAdd(&a.counters[0], n);
+      atomicAdd(&a.counters[1], n * static_cast<unsigned long long>(L.row));
+    }
+    return;
+  }
   if (lane < kNJ) {
 #pragma unroll
     for (int c = 0; c < 32; ++c)
@@ -965,7 +987,7 @@ hipError_t launch_typed(const DecodeArgs& a, int batch, hipStream_t stream) {
     hipExtLaunchKernelGGL((decode_split_kernel<D, KIND, MODE>), dim3(a.S, a.H, batch), dim3(64), 0, stream,
                           es.start, es.stop, 0, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || (a.direct_out && MODE != kModeSparse)) return e;
   const ProfEvents em = prof_events(kClassMerge);
   hipExtLaunchKernelGGL((decode_merge_kernel<D, KIND, MODE>), dim3(a.H, batch), dim3(64), 0, stream,
                         em.start, em.stop, 0, a);

@@ -43,6 +43,8 @@ struct DecodeArgs {
   int64_t num_pages;
   int32_t H, max_pages, S, split_len, mask_words;
   int32_t graded_priority;           // 1: one round of waves, see decode_split_kernel
+  int32_t direct_out;                // 1: one uniform split per pair; a plain or dense
+                                     //    split writes out itself, no merge launch
   float sm_scale;
   float log_tau;                     // ln(tau) for the candidate / flag test
   CellLayout lay;
