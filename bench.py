@@ -45,7 +45,7 @@ def parse():
                          "workloads; 0 = 64 (about 35 s of single-core work over the workers), or 40 for joint codes")
     ap.add_argument("--cpu-workers", type=int, default=16,
                     help="oracle worker processes (capped by the host's cores); 16 is one GPU's share of a box")
-    ap.add_argument("--extra", default="ragged-16k,lean-16k-p16",
+    ap.add_argument("--extra", default="ragged-16k,lean-16k-p16,ouro1.4b-4k,ouro2.6b-32k",
                     help="comma-separated workloads also timed (no oracle) and reported under 'extra'")
     ap.add_argument("--report", default=None, help="also write the JSON result to this file")
     ap.add_argument("--planner", action="store_true",
@@ -569,6 +569,18 @@ def step_spread(evs):
             "p90": float(np.percentile(d, 90))}
 
 
+def sweep_report(points):
+    """Bytes read and bandwidth at each point of a tau sweep."""
+    return [{"tau": p["tau"], "ms_per_step": p["ms_per_step"],
+             "kv_tokens_per_s": p["value"],
+             "bytes_required_per_step": p["bytes_required_per_step"],
+             "hbm_gbs_required": p["hbm_gbs_required"],
+             "split_achieved_gbs": p["split"]["achieved_gbs"],
+             "split_frac": p["split"]["achieved_gbs"] / HBM_PEAK_GBS,
+             "lo_bytes_read": p["lo_plane"]["lo_bytes_read"],
+             "lo_fraction_read": p["lo_plane"]["fraction_read"]} for p in points]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -642,17 +654,34 @@ def main():
     for name in [x for x in args.extra.split(",") if x and x != w.name]:
         ew = wl.WORKLOADS[name]
         ek, et = wl.make_plan(ew)
-        eb = Bench(args, ew, ek, et, 1)
-        r = eb.run_point()
+        # a workload with a tau sweep runs every point; its entry is the
+        # point at the workload's own plan tau, the sweep listed beside it
+        esweep = list(ew.tau_sweep) or [None]
+        eb = Bench(args, ew, ek, et, len(esweep))
+        epoints = []
+        for tau in esweep:
+            if tau is not None:
+                eb.set_tau(tau)
+            r = eb.run_point()
+            r["tau"] = "plan" if tau is None else ("inf" if math.isinf(tau) else tau)
+            esp = r["split"]
+            log(f"[bench] extra {name} tau={r['tau']}: {r['ms_per_step']:.3f} ms/step, "
+                f"split {esp['achieved_gbs']:.0f} GB/s")
+            epoints.append(r)
+        r = epoints[0]
+        if ew.tau_sweep:
+            own = float(ew.taus[0])
+            r = next(p for p in epoints if p["tau"] != "inf" and float(p["tau"]) == own)
         esp = r["split"]
         extra[name] = {"ms_per_step": r["ms_per_step"], "kv_tokens_per_s": r["value"],
                        "hbm_gbs_required": r["hbm_gbs_required"], "page": ew.page, "batch": ew.batch,
-                       "context": r["context"],
+                       "context": r["context"], "tau": r["tau"],
                        "split_roofline": {"achieved": esp["achieved_gbs"], "frac": esp["achieved_gbs"] / HBM_PEAK_GBS,
                                           "avg_launch_us": esp["ms"] * 1e3 / max(esp["launches"], 1),
                                           "launches": esp["launches"]},
                        "kernels_ms_per_step": r["kernels_ms_per_step"], "lo_plane": r["lo_plane"]}
-        log(f"[bench] extra {name}: {r['ms_per_step']:.3f} ms/step, split {esp['achieved_gbs']:.0f} GB/s")
+        if ew.tau_sweep:
+            extra[name]["tau_sweep"] = sweep_report(epoints)
         del eb
         torch.cuda.empty_cache()
     res = {
@@ -695,13 +724,7 @@ def main():
         "extra": extra,
     }
     if args.tau_sweep:
-        res["tau_sweep"] = [{"tau": p["tau"], "ms_per_step": p["ms_per_step"],
-                             "kv_tokens_per_s": p["value"],
-                             "bytes_required_per_step": p["bytes_required_per_step"],
-                             "hbm_gbs_required": p["hbm_gbs_required"],
-                             "split_achieved_gbs": p["split"]["achieved_gbs"],
-                             "lo_bytes_read": p["lo_plane"]["lo_bytes_read"],
-                             "lo_fraction_read": p["lo_plane"]["fraction_read"]} for p in points]
+        res["tau_sweep"] = sweep_report(points)
     line = json.dumps(res)
     if args.report:
         with open(args.report, "w") as f:
