@@ -685,7 +685,9 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
     {
       const int g = lane >> 5;
       const float4* qv4 = reinterpret_cast<const float4*>(qk[g]);
-      float dot = 0.0f;
+      // two interleaved sums: consecutive mixed-precision FMAs never depend
+      // on each other, so none waits for its predecessor's result
+      float dot0 = 0.0f, dot1 = 0.0f;
 #pragma unroll
       for (int k = 0; k < kWords; ++k) {
         const uint32_t hw = (&cur.kh[k / 4].x)[k % 4];
@@ -700,10 +702,10 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
         for (int v = 0; v < 4; ++v) {
           // positions 4v + b of this word: bytes 0, 1, 2, 3 of field v
           const float4 q4 = qv4[4 * k + v];
-          dot = fmaf(half_lo(pr[2 * v]), q4.x, dot);
-          dot = fmaf(half_lo(pr[2 * v + 1]), q4.y, dot);
-          dot = fmaf(half_hi(pr[2 * v]), q4.z, dot);
-          dot = fmaf(half_hi(pr[2 * v + 1]), q4.w, dot);
+          dot0 = fmaf(half_lo(pr[2 * v]), q4.x, dot0);
+          dot1 = fmaf(half_lo(pr[2 * v + 1]), q4.y, dot1);
+          dot0 = fmaf(half_hi(pr[2 * v]), q4.z, dot0);
+          dot1 = fmaf(half_hi(pr[2 * v + 1]), q4.w, dot1);
         }
         // keep each word's multiplier reads next to their use (register pressure)
         asm volatile("" ::: "memory");
@@ -711,6 +713,7 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
       }
       // computed for every lane (no branch): keeps the unrolled reads and
       // arithmetic interleaved instead of sunk into a conditional block
+      float dot = dot0 + dot1;
       asm volatile("" : "+v"(dot));
       s_t = valid ? dot + (g ? bias1 : bias0) : -INFINITY;
     }
