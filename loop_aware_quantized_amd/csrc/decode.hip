@@ -432,8 +432,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 // One split of one (sequence, head): tokens [start, end) of sequence b
 // (length T), head h; its partial record is number rec of the pair, and
 // `first` marks the split holding the pair's first token (which owns the
-// pair's mask row).
-template <int D, int KIND, int MODE>
+// pair's mask row).  kStreamed: called by the streamed-layout kernel.
+template <int D, int KIND, int MODE, bool kStreamed>
 __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, const int h, const int T,
                                               const int start, const int end, const int rec, const bool first) {
   constexpr int kNJ = D / kGroup;       // value channel groups
@@ -688,8 +688,20 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
       // two interleaved sums: consecutive mixed-precision FMAs never depend
       // on each other, so none waits for its predecessor's result
       float dot0 = 0.0f, dot1 = 0.0f;
+      // The next word's multipliers are requested while this word computes
+      // where the 16 registers that takes still leave three waves per SIMD
+      // (not in the tau = 0 variants, nor for 4-bit sources in the streamed
+      // layout); elsewhere each word's are read next to their use.
+      constexpr bool kAhead = !kDense && !(kKeyComb && kStreamed);
+      float4 mq[4], mq_next[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mq[v] = qv4[v];
 #pragma unroll
       for (int k = 0; k < kWords; ++k) {
+        if (kAhead && k + 1 < kWords) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) mq_next[v] = qv4[4 * (k + 1) + v];
+        }
         const uint32_t hw = (&cur.kh[k / 4].x)[k % 4];
         uint32_t pr[8];
         if (kKeyComb) {
@@ -701,7 +713,7 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           // positions 4v + b of this word: bytes 0, 1, 2, 3 of field v
-          const float4 q4 = qv4[4 * k + v];
+          const float4 q4 = mq[v];
           dot0 = fmaf(half_lo(pr[2 * v]), q4.x, dot0);
           dot1 = fmaf(half_lo(pr[2 * v + 1]), q4.y, dot1);
           dot0 = fmaf(half_hi(pr[2 * v]), q4.z, dot0);
@@ -710,6 +722,10 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
         // keep each word's multiplier reads next to their use (register pressure)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
+        if (k + 1 < kWords) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) mq[v] = kAhead ? mq_next[v] : qv4[4 * (k + 1) + v];
+        }
       }
       // computed for every lane (no branch): keeps the unrolled reads and
       // arithmetic interleaved instead of sunk into a conditional block
@@ -922,7 +938,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.seq_lens[b];
   const int start = split * a.split_len;
-  split_segment<D, KIND, MODE>(a, b, h, T, start, min(start + a.split_len, T), split, split == 0);
+  split_segment<D, KIND, MODE, false>(a, b, h, T, start, min(start + a.split_len, T), split, split == 0);
 }
 
 // Streamed layout: wave w takes its range of the pairs' tiles laid end to
@@ -974,7 +990,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs a) {
     const int wv = wave_of(a, t);                          // w, or a range past the grid
     const int seg = min(nb - j, min(range_start(a, wv + 1), t_end) - t);
     const int rec = wv - wave_of(a, first + h * nb);       // record number within the pair
-    split_segment<D, KIND, MODE>(a, b, h, T, j * kTile, min((j + seg) * kTile, T), rec, j == 0);
+    split_segment<D, KIND, MODE, true>(a, b, h, T, j * kTile, min((j + seg) * kTile, T), rec, j == 0);
     __syncthreads();                                       // LDS of this segment is free again
     t += seg;
   }
