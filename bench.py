@@ -45,7 +45,7 @@ def parse():
                          "workloads; 0 = 64 (about 35 s of single-core work over the workers), or 40 for joint codes")
     ap.add_argument("--cpu-workers", type=int, default=16,
                     help="oracle worker processes (capped by the host's cores); 16 is one GPU's share of a box")
-    ap.add_argument("--extra", default="ragged-16k,lean-16k-p16,ouro1.4b-4k,ouro2.6b-32k",
+    ap.add_argument("--extra", default="ragged-16k,lean-16k-p16,ouro1.4b-4k,ouro2.6b-32k,loopvq-16k",
                     help="comma-separated workloads also timed (no oracle) and reported under 'extra'")
     ap.add_argument("--report", default=None, help="also write the JSON result to this file")
     ap.add_argument("--planner", action="store_true",
@@ -427,6 +427,16 @@ def cpu_baseline(w, st, kinds, taus, n_samples, dev, workers):
 
 
 def vq_main(args, w):
+    """Bench of a LoopVQ-style workload, printed as the JSON line."""
+    res = vq_run(args, w, with_cpu=not args.no_cpu_baseline)
+    line = json.dumps(res)
+    if args.report:
+        with open(args.report, "w") as f:
+            f.write(line + "\n")
+    print(line, flush=True)
+
+
+def vq_run(args, w, with_cpu):
     """Bench of a LoopVQ-style workload: per step, every layer codes one
     appended token (all loops jointly) and every (loop, layer) cell decodes."""
     import torch
@@ -493,7 +503,7 @@ def vq_main(args, w):
     n_split, split_ms = kst["split"]
     achieved = split_bytes / (split_ms / 1e3) / 1e9
     stored = L * abi.vq_pool_bytes(st.dims, st.num_pages)
-    cpu = None if args.no_cpu_baseline else vq_cpu_baseline(w, st, queries, n_samples=args.cpu_samples or 40)
+    cpu = vq_cpu_baseline(w, st, queries, n_samples=args.cpu_samples or 40) if with_cpu else None
     res = {
         "metric": METRIC, "value": tokens * R * L / (ms / 1e3), "unit": "KV tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -512,11 +522,9 @@ def vq_main(args, w):
         "storage": {"stored_bytes": stored},
         "cpu_baseline": cpu,
     }
-    line = json.dumps(res)
-    if args.report:
-        with open(args.report, "w") as f:
-            f.write(line + "\n")
-    print(line, flush=True)
+    del st
+    torch.cuda.empty_cache()
+    return res
 
 
 def vq_cpu_baseline(w, st, queries, n_samples):
@@ -652,6 +660,19 @@ def main():
     torch.cuda.empty_cache()
     extra = {}
     for name in [x for x in args.extra.split(",") if x and x != w.name]:
+        if name in wl.VQ_WORKLOADS:
+            r = vq_run(args, wl.VQ_WORKLOADS[name], with_cpu=False)
+            extra[name] = {"ms_per_step": r["ms_per_step"], "kv_tokens_per_s": r["value"],
+                           "hbm_gbs_required": r["hbm_gbs_required"], "page": r["config"]["page"],
+                           "batch": r["config"]["batch"], "context": r["config"]["context"],
+                           "bits_per_element": r["config"]["bits_per_element"],
+                           "split_roofline": {k: r["roofline"][k] for k in ("kernel", "achieved", "frac",
+                                                                            "avg_launch_us", "launches")},
+                           "kernels_ms_per_step": r["kernels_ms_per_step"], "storage": r["storage"]}
+            log(f"[bench] extra {name}: {r['ms_per_step']:.3f} ms/step, "
+                f"{r['roofline']['kernel']} {r['roofline']['achieved']:.0f} GB/s")
+            torch.cuda.empty_cache()
+            continue
         ew = wl.WORKLOADS[name]
         ek, et = wl.make_plan(ew)
         # a workload with a tau sweep runs every point; its entry is the
