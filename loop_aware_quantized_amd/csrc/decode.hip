@@ -719,7 +719,9 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
           dot0 = fmaf(half_hi(pr[2 * v]), q4.z, dot0);
           dot1 = fmaf(half_hi(pr[2 * v + 1]), q4.w, dot1);
         }
-        // keep each word's multiplier reads next to their use (register pressure)
+        // each word's work stays together (register pressure): no later
+        // word's multiplier reads or unpacking move into it, beyond the
+        // next word's reads requested above
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         if (k + 1 < kWords) {
