@@ -30,3 +30,22 @@ def test_planner_report_lines():
         assert k["q4"] + k["q2"] + k["reuse"] == x["cells"]
         assert x["damage"] <= x["damage_budget"] * (1 + 1e-12)
         assert x["storage_units"] <= x["storage_budget_units"]
+
+
+def test_default_extra_workloads_exist(monkeypatch):
+    """Every workload the default run times beside the primary one is a known
+    workload (a misspelt name would only fail on the GPU, after the primary
+    line's timing)."""
+    monkeypatch.syspath_prepend(ROOT)
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    import bench
+    from loop_aware_quantized_amd import inputs as wl
+    names = [x for x in bench.parse().extra.split(",") if x]
+    assert names, "the default run times extra workloads"
+    for n in names:
+        assert n in wl.WORKLOADS or n in wl.VQ_WORKLOADS, n
+    # a swept workload's entry is its own plan tau, which must be a sweep point
+    for n in names:
+        w = wl.WORKLOADS.get(n)
+        if w is not None and w.tau_sweep:
+            assert float(w.taus[0]) in [float(t) for t in w.tau_sweep]
