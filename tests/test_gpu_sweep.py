@@ -1,0 +1,81 @@
+"""GPU parity over a seeded random sweep of small configurations.
+
+Each case draws its own shape (head dim, page size, heads, loops, layers,
+batch), ragged lengths (with the edge lengths 0, 1, 63, 64 and 65 mixed in),
+a plan (reuse only before the final loop), per-cell tau from the fast paths
+and the sparse range, page shuffling, heavy-token fraction, split count and
+whether the length-sum hint is given, then checks every stored pool byte and
+every decoded cell against the oracle (parity bar of tests/parity_util.py).
+The draws come from numpy's seeded generator, so a case is reproduced by its
+number alone.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oa
+from loop_aware_quantized_amd import inputs as wl
+from loop_aware_quantized_amd import runner
+from parity_util import check_pool, compare_decode, say, tau_str
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0) if torch.cuda.is_available() else None
+Q4, Q2, RU = wl.KIND_Q4, wl.KIND_Q2, wl.KIND_REUSE
+TAUS = [0.0, 1e-3, 5e-3, 0.02, 0.1, math.inf]
+EDGE_LENS = [0, 1, 63, 64, 65]
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def draw_case(case: int):
+    """Shape, lengths, plan and decode options of sweep case `case`."""
+    rng = np.random.default_rng([7, case])
+    D = int(rng.choice([64, 128]))
+    P = int(rng.choice([16, 32, 64]))
+    H = int(rng.integers(1, 6))
+    R = int(rng.integers(1, 4))
+    L = int(rng.integers(1, 4))
+    B = int(rng.integers(1, 9))
+    lens = [int(x) for x in rng.integers(0, 6001, size=B)]
+    for i in range(B):
+        if rng.random() < 0.3:
+            lens[i] = int(rng.choice(EDGE_LENS))
+    kinds = [[int(rng.choice([Q4, Q2, RU] if r < R - 1 else [Q4, Q2])) for _ in range(L)] for r in range(R)]
+    taus = [[float(rng.choice(TAUS)) for _ in range(L)] for _ in range(R)]
+    opts = dict(shuffle=bool(rng.random() < 0.5), heavy=float(rng.choice([0.0, 0.01, 0.05])),
+                splits=int(rng.choice([0, 0, 1, 2, 5])), hint=bool(rng.random() < 0.7))
+    return D, P, H, R, L, B, lens, kinds, taus, opts
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_random_configuration(case):
+    D, P, H, R, L, B, lens, kinds, taus, o = draw_case(case)
+    say(f"sweep case {case}: D={D} P={P} H={H} R={R} L={L} B={B} lens={lens} kinds={kinds} "
+        f"taus={[[tau_str(t) for t in row] for row in taus]} {o}")
+    w = wl.Workload(f"sweep-{case}", 300 + case, batch=B, loops=R, layers=L, heads=H, head_dim=D, page=P,
+                    ctx=max(max(lens), 1), heavy_frac=o["heavy"], shuffle_pages=o["shuffle"])
+    st = runner.CacheState(w, DEV, kinds, taus, lengths=lens)
+    kept = st.prefill({c: set(range(B)) for c in st.stored})
+    torch.cuda.synchronize()
+    for (r, l) in st.stored:
+        for b in range(B):
+            if lens[b] > 0:                  # an empty sequence stores nothing
+                check_pool(st, r, l, b, *kept[(r, l)][b])
+    for r in range(R):
+        for l in range(L):
+            q = wl.cell_query(w, st.cell_index(r, l), DEV)[1]
+            out = torch.empty(B, H, D, dtype=torch.float32, device=DEV)
+            mask = st.new_mask()
+            st.decode(r, l, q, out, num_splits=o["splits"], mask=mask,
+                      sum_seq_lens=None if o["hint"] else 0)
+            torch.cuda.synchronize()
+            src = oa.resolve_source(st.kinds, r, l)
+            s = compare_decode(st, r, l, q, out, mask, kept[src], range(B))
+            say(f"  cell ({r},{l}) src {src} tau {tau_str(taus[r][l])}: rel err {s['rel']:.2e} "
+                f"flagged {s['flagged']} band {s['band']}")
