@@ -116,3 +116,27 @@ def test_streamed_layout_of_the_ragged_16k_shape():
     lens = [int(x) for x in wl.make_lengths(w)]
     waves, S = _check(lens, w.heads, sum(lens))
     assert waves > SLOTS and S >= 2
+
+
+def test_gpu_sweep_covers_every_layout():
+    """The seeded GPU parity sweep (tests/test_gpu_sweep.py) decodes in the
+    streamed layout, in uniform splits and in a single split per pair, so a
+    change of the split choice cannot leave one of them untested there."""
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location(
+        "gpu_sweep_cases", os.path.join(os.path.dirname(os.path.abspath(__file__)), "test_gpu_sweep.py"))
+    sweep = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(sweep)
+    seen = {"streamed": 0, "uniform": 0, "one split": 0}
+    n_cases = len(sweep.test_random_configuration.pytestmark[0].args[1])
+    for case in range(n_cases):
+        D, P, H, R, L, B, lens, kinds, taus, o = sweep.draw_case(case)
+        plan = abi.Plan(abi.plan_blob(R, L, H, D, P, np.array(kinds), np.array(taus)))
+        hint = sum(lens) if o["hint"] else 0
+        for r in range(R):
+            for l in range(L):
+                streamed, S, _, _ = abi.loopkv_decode_layout(plan, r, l, B, max(max(lens), 1), hint,
+                                                             o["splits"])
+                seen["streamed" if streamed else ("one split" if S == 1 else "uniform")] += 1
+    assert all(v >= 5 for v in seen.values()), seen
