@@ -206,11 +206,13 @@ def make_block_tables(w: Workload, capacity, extra_pages: int = 0):
     Returns (table int32 [B][max_pages], num_pages).  Sequences own disjoint
     physical pages; a shuffled workload draws them as a random permutation of
     the pool, otherwise they are contiguous and in order.  Unused entries are
-    0 (never dereferenced).  ``extra_pages`` spare pages end the pool.
+    0 (never dereferenced).  ``extra_pages`` spare pages end the pool, which
+    holds at least one page (the library takes no empty pool, even for a
+    batch of empty sequences).
     """
     capacity = np.asarray(capacity, np.int64)
     pages = (capacity + w.page - 1) // w.page
-    total = int(pages.sum()) + int(extra_pages)
+    total = max(1, int(pages.sum()) + int(extra_pages))
     max_pages = int(max(1, pages.max()))
     phys = np.arange(total, dtype=np.int64)
     if w.shuffle_pages:

@@ -68,6 +68,8 @@ class CacheState:
         w = self.w
         cell = self.cell_index(r, l)
         kept = {}
+        if np.all(self.lens0 == 0):
+            return kept                      # nothing to store
         if np.all(self.lens0 == self.lens0[0]):
             T = int(self.lens0[0])
             K, V = wl.cell_kv(w, cell, T, self.device)

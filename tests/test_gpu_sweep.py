@@ -79,3 +79,22 @@ def test_random_configuration(case):
             s = compare_decode(st, r, l, q, out, mask, kept[src], range(B))
             say(f"  cell ({r},{l}) src {src} tau {tau_str(taus[r][l])}: rel err {s['rel']:.2e} "
                 f"flagged {s['flagged']} band {s['band']}")
+
+
+def test_all_sequences_empty():
+    """A batch whose every sequence is empty decodes to zeros in every mode
+    (4-bit sparse, dense and plain, 2-bit, reuse) and sets no mask bit."""
+    w = wl.Workload("all-empty", 350, batch=3, loops=2, layers=3, heads=2, head_dim=128, page=16, ctx=1)
+    kinds = [[Q4, Q2, RU], [Q4, Q4, Q2]]
+    taus = [[0.01, 0.01, 0.0], [0.0, math.inf, 0.02]]
+    st = runner.CacheState(w, DEV, kinds, taus, lengths=[0, 0, 0])
+    st.prefill({c: set() for c in st.stored})
+    for r in range(2):
+        for l in range(3):
+            q = wl.cell_query(w, st.cell_index(r, l), DEV)[1]
+            out = torch.full((3, 2, 128), float("nan"), dtype=torch.float32, device=DEV)
+            mask = st.new_mask()
+            st.decode(r, l, q, out, mask=mask)
+            torch.cuda.synchronize()
+            assert torch.count_nonzero(out) == 0, (r, l)
+            assert mask.numel() == 0 or torch.count_nonzero(mask) == 0, (r, l)
