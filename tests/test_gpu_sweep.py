@@ -16,6 +16,7 @@ import pytest
 import torch
 
 from oracle import attention as oa
+from loop_aware_quantized_amd import abi
 from loop_aware_quantized_amd import inputs as wl
 from loop_aware_quantized_amd import runner
 from parity_util import check_pool, compare_decode, say, tau_str
@@ -98,3 +99,56 @@ def test_all_sequences_empty():
             torch.cuda.synchronize()
             assert torch.count_nonzero(out) == 0, (r, l)
             assert mask.numel() == 0 or torch.count_nonzero(mask) == 0, (r, l)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_append_random_schedules(case):
+    """Random starting lengths per sequence, then a random schedule of
+    appends (1 to 70 tokens per call, the same count for every sequence from
+    its own length), crossing key groups and pages: every pool byte equals
+    the oracle's packing of the whole sequence, and decodes match."""
+    rng = np.random.default_rng([13, case])
+    D = int(rng.choice([64, 128]))
+    P = int(rng.choice([16, 32, 64]))
+    H = int(rng.integers(1, 4))
+    B = int(rng.integers(1, 5))
+    start = rng.integers(0, 201, size=B).astype(np.int32)
+    steps = [int(rng.choice([1, 1, 1, 2, 5, 31, 32, 33, 70])) for _ in range(int(rng.integers(1, 7)))]
+    final = start + sum(steps)
+    taus = [[float(rng.choice(TAUS)), float(rng.choice(TAUS))]]
+    say(f"append case {case}: D={D} P={P} H={H} B={B} start={start.tolist()} steps={steps}")
+    w = wl.Workload(f"append-sweep-{case}", 360 + case, batch=B, loops=1, layers=2, heads=H, head_dim=D, page=P,
+                    ctx=int(final.max()), heavy_frac=0.02, shuffle_pages=bool(rng.random() < 0.5))
+    st = runner.CacheState(w, DEV, [[Q4, Q2]], taus, lengths=final)
+    T = int(final.max())
+    kept = {}
+    for (r, l) in st.stored:
+        K, V = wl.cell_kv(w, st.cell_index(r, l), T, DEV)
+        for bi in range(B):
+            n0 = int(start[bi])
+            if n0:
+                lens = torch.zeros(1, dtype=torch.int32, device=DEV)
+                batch = abi.make_batch(lens, st.block_tables[bi:bi + 1], st.max_seq_len,
+                                       slots=st.slots[bi:bi + 1])
+                abi.loopkv_append(st.plan, st.cells, r, l, batch, n0, K[bi:bi + 1, :n0].contiguous(),
+                                  V[bi:bi + 1, :n0].contiguous())
+        cur = start.copy()
+        for n in steps:
+            idx = torch.from_numpy((cur[:, None] + np.arange(n)[None, :]).astype(np.int64)).to(DEV)
+            kk = torch.stack([K[bi, idx[bi]] for bi in range(B)])
+            vv = torch.stack([V[bi, idx[bi]] for bi in range(B)])
+            st.append(r, l, kk, vv, torch.from_numpy(cur).to(DEV))
+            cur = cur + n
+        kept[(r, l)] = {bi: (wl.bf16_bits(K[bi, :int(final[bi])]), wl.bf16_bits(V[bi, :int(final[bi])]))
+                        for bi in range(B)}
+    torch.cuda.synchronize()
+    for (r, l) in st.stored:
+        for bi in range(B):
+            check_pool(st, r, l, bi, *kept[(r, l)][bi])
+    for l in range(2):
+        q = wl.cell_query(w, st.cell_index(0, l), DEV)[1]
+        out = torch.empty(B, H, D, dtype=torch.float32, device=DEV)
+        mask = st.new_mask()
+        st.decode(0, l, q, out, mask=mask)
+        torch.cuda.synchronize()
+        compare_decode(st, 0, l, q, out, mask, kept[(0, l)], range(B))
