@@ -680,7 +680,8 @@ int decode_impl(const char* who, const loopkv_plan* plan, const loopkv_cell_mem*
   a.batch = batch->batch;
   a.cand_stride = static_cast<int32_t>(sp.cand_stride);
   const int64_t waves = sp.streamed ? sp.waves : static_cast<int64_t>(sp.S) * plan->H * batch->batch;
-  a.graded_priority = waves <= static_cast<int64_t>(cu_count()) * 12;
+  // one round of resident waves (3 per SIMD): issue priority is graded by progress and dispatch rank
+  a.grade_simds = waves <= static_cast<int64_t>(cu_count()) * 12 ? cu_count() * 4 : 0;
   // one split per pair and no tau test: the split writes the output itself
   a.direct_out = (!sp.streamed && sp.S == 1 && mode != lkv::kModeSparse) ? 1 : 0;
   a.mask_words = (batch->max_seq_len + 31) / 32;

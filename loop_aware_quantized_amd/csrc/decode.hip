@@ -853,11 +853,16 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
   };
 
   // When all splits run in one round of resident waves, issue priority
-  // falls as a split progresses (3 in its first quarter, 0 in its last).
+  // falls as a split progresses (3, 2, 1 in its first three quarters).
   // Waves sharing a SIMD otherwise issue oldest-first, and with equal splits
   // the youngest finish up to 1.6x later than the oldest; handing priority
   // to the waves that are behind shortens that tail (measured: 3-4% per
-  // launch).  Launches of several rounds refill freed slots instead.
+  // launch).  In its last quarter a wave's priority is its dispatch rank on
+  // its SIMD, so that among waves near their end the youngest, which is
+  // behind, issues first instead of the oldest (1-1.5% per step more).  The
+  // dispatcher places one wave per SIMD in block order, so the rank is the
+  // linear block index over the SIMD count.  Launches of several rounds
+  // refill freed slots instead.
   auto set_priority = [](int p) {
     switch (p) {
       case 0: __builtin_amdgcn_s_setprio(0); break;
@@ -868,11 +873,16 @@ __device__ __forceinline__ void split_segment(const DecodeArgs& a, const int b, 
   };
   const int n_tiles = (end - start + kTile - 1) / kTile;
   int tiles_done = 0;
+  const int lin_block = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int rank = a.grade_simds ? min(3, lin_block / a.grade_simds) : 0;
   auto progress = [&]() {
     ++tiles_done;
-    if (a.graded_priority) set_priority(3 - min(3, (4 * tiles_done) / n_tiles));
+    if (a.grade_simds) {
+      const int q = (4 * tiles_done) / n_tiles;
+      set_priority(q >= 3 ? rank : 3 - q);
+    }
   };
-  if (a.graded_priority) set_priority(3);
+  if (a.grade_simds) set_priority(3);
 
   // ping-pong over two tile buffers: the next tile's loads are issued before
   // the current tile computes.  A tile with no successor issues the same

@@ -42,7 +42,9 @@ struct DecodeArgs {
   unsigned long long* counters;      // optional [2]
   int64_t num_pages;
   int32_t H, max_pages, S, split_len, mask_words;
-  int32_t graded_priority;           // 1: one round of waves, see decode_split_kernel
+  int32_t grade_simds;               // one round of waves: the chip's SIMD count (block b is
+                                     //    dispatched as wave b / grade_simds of its SIMD);
+                                     //    0: several rounds, no issue-priority grading
   int32_t direct_out;                // 1: one uniform split per pair; a plain or dense
                                      //    split writes out itself, no merge launch
   float sm_scale;
