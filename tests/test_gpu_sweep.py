@@ -80,6 +80,17 @@ def test_random_configuration(case):
             s = compare_decode(st, r, l, q, out, mask, kept[src], range(B))
             say(f"  cell ({r},{l}) src {src} tau {tau_str(taus[r][l])}: rel err {s['rel']:.2e} "
                 f"flagged {s['flagged']} band {s['band']}")
+            # the allocation-free entry point runs the same kernels and layout:
+            # the same bits, whenever the batch fits its fixed scratch
+            hint = int(st.lens0.sum()) if o["hint"] else 0
+            if abi.loopkv_decode_noalloc_bytes(st.plan, r, l, B, st.max_seq_len, hint, o["splits"]) \
+                    <= abi.NOALLOC_SCRATCH_BYTES:
+                out2 = torch.full_like(out, float("nan"))
+                mask2 = st.new_mask()
+                opts = abi.make_opts(None, mask_bits=mask2, num_splits=o["splits"])
+                abi.loopkv_decode_noalloc(st.plan, st.cells, r, l, st.batch(sum_seq_lens=hint), q, out2, opts)
+                torch.cuda.synchronize()
+                assert torch.equal(out, out2) and torch.equal(mask, mask2), (r, l)
 
 
 def test_all_sequences_empty():
